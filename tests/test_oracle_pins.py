@@ -1,0 +1,352 @@
+"""Pins of the fp64 CPU oracle to facts the pages and the mathematics fix.
+
+None of these compare the oracle with itself: each checks a closed form, a
+special case, an invariant, a value printed on a page, or an independent
+formulation (exact rationals, the matrix form of the step, explicit products).
+"""
+import json
+import math
+import os
+from fractions import Fraction as Fr
+
+import numpy as np
+import pytest
+
+from oracle import chunked, exact
+from oracle import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    from oracle import build
+    build.build(force=False)
+
+
+# ------------------------------------------------------------------ gate --
+
+def test_gate_zero_preactivation_gives_half():
+    # softplus(0) = ln 2, a_log = 0 -> la = -ln 2, alpha = 1/2
+    dtb = np.array([0.25, -1.5, 3.0])
+    raw = -dtb[None, :].repeat(2, axis=0)
+    la = orc.log_alpha(raw, dtb, 0.0)
+    assert np.allclose(la, -math.log(2.0), rtol=0, atol=1e-15)
+    la3 = orc.log_alpha(raw, dtb, math.log(3.0))
+    assert np.allclose(la3, -3.0 * math.log(2.0), rtol=1e-15, atol=0)
+
+
+def test_gate_softplus_identity_and_asymptotes():
+    rng = np.random.default_rng(1)
+    x = rng.normal(0, 6, size=(50, 4))
+    zero = np.zeros(4)
+    A = 2.5
+    la_p = orc.log_alpha(x, zero, math.log(A))
+    la_m = orc.log_alpha(-x, zero, math.log(A))
+    # softplus(x) - softplus(-x) = x
+    assert np.allclose(la_p - la_m, -A * x, rtol=1e-13, atol=1e-13)
+    big = np.full((1, 4), 40.0)
+    assert np.allclose(orc.log_alpha(big, zero, 0.0), -40.0, rtol=1e-15)
+    small = np.full((1, 4), -40.0)
+    assert np.allclose(orc.log_alpha(small, zero, 0.0), -math.exp(-40.0), rtol=1e-12)
+
+
+def test_safe_gate_clamps_only_below_bound():
+    rng = np.random.default_rng(2)
+    x = rng.normal(0, 3, size=(200, 8))
+    dtb = rng.normal(0, 0.1, size=8)
+    orig = orc.log_alpha(x, dtb, math.log(16.0), gate_mode=0)
+    safe = orc.log_alpha(x, dtb, math.log(16.0), gate_mode=1, lb=-5.0)
+    assert (orig < -5).any() and (orig > -5).any()
+    assert np.array_equal(safe, np.maximum(orig, -5.0))
+
+
+def test_beta_sigmoid_and_probability():
+    x = np.array([0.0, 1.0, -1.0, 7.5, -7.5])
+    b = orc.beta(x, 0)
+    assert b[0] == 0.5
+    assert np.allclose(b[1:3].sum(), 1.0, atol=1e-15) and np.allclose(b[3:].sum(), 1.0, atol=1e-15)
+    assert np.allclose(b[1], 1 / (1 + math.exp(-1.0)), rtol=1e-15)
+    assert np.array_equal(orc.beta(x, 1), x)
+
+
+# ------------------------------------------------------------ recurrence --
+
+def _rand(rng, n, dk, dv):
+    k = rng.normal(size=(n, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q = rng.normal(size=(n, dk))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    v = rng.normal(size=(n, dv))
+    alpha = rng.uniform(0.3, 1.0, size=(n, dk))
+    beta = rng.uniform(0.05, 0.95, size=n)
+    S0 = rng.normal(size=(dk, dv))
+    return q, k, v, alpha, beta, S0
+
+
+def test_beta_zero_alpha_one_leaves_state_unchanged():
+    rng = np.random.default_rng(3)
+    q, k, v, _, _, S0 = _rand(rng, 9, 5, 3)
+    out, S = orc.recur(k, v, np.ones((9, 5)), np.zeros(9), S0, q=q, scale=0.7)
+    assert np.array_equal(S, S0)                         # bit-exact
+    assert np.allclose(out, 0.7 * q @ S0, rtol=1e-14, atol=1e-14)
+
+
+def test_same_unit_key_written_twice_overwrites_not_doubles():
+    dk, dv = 4, 3
+    e = np.zeros(dk)
+    e[2] = 1.0
+    v1 = np.array([1.0, -2.0, 0.5])
+    v2 = np.array([3.0, 0.25, -1.0])
+    for vals in ([v1, v1], [v1, v2]):
+        _, S = orc.recur(np.stack([e, e]), np.stack(vals), np.ones((2, dk)), np.ones(2),
+                         np.zeros((dk, dv)))
+        assert np.allclose(e @ S, vals[-1], atol=2e-16)  # not 2*v1, not v1+v2
+        assert np.array_equal(np.delete(S, 2, axis=0), np.zeros((dk - 1, dv)))
+
+
+def test_alpha_zero_forgets_everything():
+    rng = np.random.default_rng(4)
+    q, k, v, _, beta, S0 = _rand(rng, 6, 4, 5)
+    out, S = orc.recur(k, v, np.zeros((6, 4)), beta, S0, q=q, scale=0.5)
+    assert np.allclose(S, beta[-1] * np.outer(k[-1], v[-1]), atol=1e-15)
+    closed = 0.5 * beta[:, None] * (q * k).sum(1)[:, None] * v
+    assert np.allclose(out, closed, atol=1e-15)
+
+
+def test_orthonormal_keys_write_rows():
+    rng = np.random.default_rng(5)
+    dk, dv, n = 4, 3, 6
+    k = np.eye(dk)[np.arange(n) % dk]
+    v = rng.normal(size=(n, dv))
+    S0 = rng.normal(size=(dk, dv))
+    _, S = orc.recur(k, v, np.ones((n, dk)), np.ones(n), S0)
+    want = S0.copy()
+    for t in range(n):
+        want[t % dk] = v[t]
+    assert np.allclose(S, want, atol=1e-15)
+    _, S3 = orc.recur(k[:3], v[:3], np.ones((3, dk)), np.ones(3), S0)
+    assert np.array_equal(S3[3], S0[3])                  # unwritten row untouched
+
+
+def test_decay_acts_on_key_rows():
+    rng = np.random.default_rng(6)
+    dk, dv, n = 3, 5, 4
+    alpha = rng.uniform(0.1, 1.0, size=(n, dk))
+    S0 = rng.normal(size=(dk, dv))
+    _, S = orc.recur(rng.normal(size=(n, dk)), rng.normal(size=(n, dv)), alpha, np.zeros(n), S0)
+    assert np.allclose(S, alpha.prod(0)[:, None] * S0, rtol=1e-14)
+
+
+def test_prediction_reads_the_decayed_state():
+    # k = e0, beta = 1: the decayed row is predicted exactly, so row 0 becomes v
+    S0 = np.array([[2.0, -4.0], [1.0, 1.0]])
+    alpha = np.array([[0.5, 0.25]])
+    v = np.array([[7.0, 9.0]])
+    _, S = orc.recur(np.array([[1.0, 0.0]]), v, alpha, np.ones(1), S0)
+    assert np.array_equal(S[0], v[0])
+    assert np.array_equal(S[1], 0.25 * S0[1])
+
+
+def test_readout_uses_updated_state():
+    # from the zero state one token reads what it just wrote
+    k = np.array([[0.6, 0.8]])
+    q = np.array([[0.8, 0.6]])
+    v = np.array([[1.0, -3.0, 2.0]])
+    out, _ = orc.recur(k, v, np.ones((1, 2)), np.array([0.5]), np.zeros((2, 3)), q=q, scale=2.0)
+    assert np.allclose(out[0], 2.0 * 0.5 * (0.48 + 0.48) * v[0], atol=1e-15)
+
+
+def test_scalar_state_closed_form():
+    rng = np.random.default_rng(7)
+    n = 20
+    k = rng.normal(size=(n, 1))
+    v = rng.normal(size=(n, 1))
+    a = rng.uniform(0.5, 1.0, size=(n, 1))
+    b = rng.uniform(0, 1, size=n)
+    s = 0.3
+    for t in range(n):
+        s = (1 - b[t] * k[t, 0] ** 2) * a[t, 0] * s + b[t] * k[t, 0] * v[t, 0]
+    _, S = orc.recur(k, v, a, b, np.array([[0.3]]))
+    assert np.allclose(S[0, 0], s, rtol=1e-13)
+
+
+def test_matches_matrix_form_of_the_step():
+    # S_t = (I - b k k^T) Diag(alpha) S_{t-1} + b k v^T ; o_t = scale q^T S_t
+    rng = np.random.default_rng(8)
+    q, k, v, alpha, beta, S0 = _rand(rng, 12, 6, 4)
+    S = S0.copy()
+    outs = []
+    for t in range(12):
+        S = (np.eye(6) - beta[t] * np.outer(k[t], k[t])) @ np.diag(alpha[t]) @ S \
+            + beta[t] * np.outer(k[t], v[t])
+        outs.append(0.3 * q[t] @ S)
+    out, Sf = orc.recur(k, v, alpha, beta, S0, q=q, scale=0.3)
+    assert np.allclose(Sf, S, rtol=1e-12, atol=1e-13)
+    assert np.allclose(out, np.array(outs), rtol=1e-12, atol=1e-13)
+
+
+def test_matches_exact_rationals():
+    rng = np.random.default_rng(9)
+    n, dk, dv = 6, 3, 2
+
+    def dy(shape, lo, hi, den=16):   # dyadic rationals: exact in fp64
+        return rng.integers(lo, hi, size=shape) / den
+
+    q, k, v = dy((n, dk), -16, 17), dy((n, dk), -16, 17), dy((n, dv), -32, 33)
+    alpha, beta, S0 = dy((n, dk), 4, 17), dy(n, 0, 17), dy((dk, dv), -16, 17)
+    eo, eS = exact.exact_forward(q.tolist(), k.tolist(), v.tolist(), alpha.tolist(),
+                                 beta.tolist(), S0.tolist(), scale=Fr(1, 2))
+    out, S = orc.recur(k, v, alpha, beta, S0, q=q, scale=0.5)
+    assert np.allclose(S, np.array(eS, dtype=float), rtol=1e-13, atol=1e-14)
+    assert np.allclose(out, np.array(eo, dtype=float), rtol=1e-13, atol=1e-14)
+
+
+def test_forward_items_equals_gate_then_recurrence_threads():
+    rng = np.random.default_rng(10)
+    dk, dv = 8, 5
+    items, want = [], []
+    for n in (1, 7, 33):
+        raw = rng.normal(size=(n, dk))
+        dtb = rng.normal(0, 0.1, size=dk)
+        logits = rng.normal(size=n)
+        q, k, v, _, _, S0 = _rand(rng, n, dk, dv)
+        al = rng.uniform(0, math.log(16))
+        items.append(dict(q=q, k=k, v=v, raw_gate=raw, beta_in=logits, dt_bias=dtb, a_log=al, S0=S0))
+        la = orc.log_alpha(raw, dtb, al, 1, -5.0)
+        want.append(orc.recur(k, v, np.exp(la), orc.beta(logits), S0, q=q, scale=0.25))
+    got = orc.forward_items(items, dk, dv, 1, -5.0, 0, 0.25, nthreads=3)
+    for (o, S), (wo, wS) in zip(got, want):
+        assert np.allclose(S, wS, rtol=1e-13, atol=1e-15) and np.allclose(o, wo, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------ chunk form --
+
+@pytest.mark.parametrize("chunk", [1, 2, 5, 16, 64])
+def test_chunk_form_equals_recurrence(chunk):
+    rng = np.random.default_rng(11)
+    n, dk, dv = 150, 16, 12
+    q, k, v, _, beta, S0 = _rand(rng, n, dk, dv)
+    la = -rng.uniform(0.0, 1.5, size=(n, dk))
+    out_r, S_r = orc.recur(k, v, np.exp(la), beta, S0, q=q, scale=0.25)
+    out_c, S_c = chunked.chunked_forward(q, k, v, la, beta, S0, chunk=chunk, scale=0.25)
+    assert np.max(np.abs(out_c - out_r)) <= 1e-12 * max(1.0, np.max(np.abs(out_r)))
+    assert np.max(np.abs(S_c - S_r)) <= 1e-12 * max(1.0, np.max(np.abs(S_r)))
+
+
+def test_chunk_form_survives_strong_decay():
+    # log-alpha down to -5 per token over a 64-token chunk: exp(G) reaches e^-320
+    rng = np.random.default_rng(12)
+    n, dk, dv = 130, 8, 4
+    q, k, v, _, beta, S0 = _rand(rng, n, dk, dv)
+    la = -rng.uniform(0.0, 5.0, size=(n, dk))
+    out_r, S_r = orc.recur(k, v, np.exp(la), beta, S0, q=q)
+    out_c, S_c = chunked.chunked_forward(q, k, v, la, beta, S0, chunk=64)
+    assert np.all(np.isfinite(out_c)) and np.all(np.isfinite(S_c))
+    assert np.allclose(out_c, out_r, rtol=1e-10, atol=1e-12)
+    assert np.allclose(S_c, S_r, rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------- segment maps --
+
+def _seg_item(rng, n, dk, dv):
+    q, k, v, _, _, _ = _rand(rng, n, dk, dv)
+    return dict(k=k, v=v, raw_gate=rng.normal(size=(n, dk)), beta_in=rng.normal(size=n),
+                dt_bias=rng.normal(0, 0.1, size=dk), a_log=rng.uniform(0, math.log(4)))
+
+
+def test_segment_map_is_the_explicit_token_product():
+    rng = np.random.default_rng(13)
+    dk, dv, n = 5, 3, 9
+    it = _seg_item(rng, n, dk, dv)
+    (M, U), = orc.segment_maps([it], dk, dv, 0, -5.0, 0)
+    alpha = np.exp(orc.log_alpha(it["raw_gate"], it["dt_bias"], it["a_log"]))
+    beta = orc.beta(it["beta_in"])
+    P = np.eye(dk)
+    Uw = np.zeros((dk, dv))
+    for t in range(n):   # later tokens multiply on the left
+        step = (np.eye(dk) - beta[t] * np.outer(it["k"][t], it["k"][t])) @ np.diag(alpha[t])
+        P = step @ P
+        Uw = step @ Uw + beta[t] * np.outer(it["k"][t], it["v"][t])
+    assert np.allclose(M, P, rtol=1e-13, atol=1e-15)
+    assert np.allclose(U, Uw, rtol=1e-13, atol=1e-15)
+
+
+def test_segment_map_is_affine_in_the_incoming_state():
+    rng = np.random.default_rng(14)
+    dk, dv, n = 6, 4, 25
+    it = _seg_item(rng, n, dk, dv)
+    (M, U), = orc.segment_maps([it], dk, dv, 0, -5.0, 0)
+    for _ in range(3):
+        S_in = rng.normal(size=(dk, dv))
+        (_, S_out), = orc.forward_items([dict(it, q=None, S0=S_in)], dk, dv, 0, -5.0, 0, 1.0)
+        assert np.allclose(S_out, M @ S_in + U, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------- scan --
+
+def _golden():
+    with open(os.path.join(GOLDEN, "scalar_three_segment.json")) as f:
+        return json.load(f)
+
+
+def test_scan_reproduces_scalar_example():
+    g = _golden()
+    M = np.array(g["M"]).reshape(3, 1, 1)
+    U = np.array(g["U"]).reshape(3, 1, 1)
+    r = orc.scan(M, U, np.array([[g["S_init"]]]))
+    assert set(r) == {"incoming_states", "outgoing_states", "final_state"}
+    assert r["incoming_states"].ravel().tolist() == g["incoming_states"]
+    assert r["outgoing_states"].ravel().tolist() == g["outgoing_states"]
+    assert r["final_state"].ravel().tolist() == [g["final_state"]]
+    # composing the first two segments in order reproduces the second outgoing state
+    r2 = orc.scan(M[:2], U[:2], np.array([[g["S_init"]]]))
+    assert r2["final_state"][0, 0] == g["compose_F1_after_F0_applied_to_initial"]
+    # the two-segment scans, as maps of the initial state, give (6,3) and the reverse (6,1)
+    for order, want in (([0, 1], g["compose_F1_after_F0"]), ([1, 0], g["compose_F0_after_F1"])):
+        f0 = orc.scan(M[order], U[order], np.zeros((1, 1)))["final_state"][0, 0]
+        f1 = orc.scan(M[order], U[order], np.ones((1, 1)))["final_state"][0, 0]
+        assert [f1 - f0, f0] == want
+
+
+def test_scan_is_not_any_listed_mistake():
+    g = _golden()
+    M = np.array(g["M"]).reshape(3, 1, 1)
+    U = np.array(g["U"]).reshape(3, 1, 1)
+    inc = orc.scan(M, U, np.array([[1.0]]))["incoming_states"].ravel().tolist()
+    assert inc != [3.0, 9.0, 5.0]          # inclusive prefix
+    assert inc != [0.0, 1.0, 3.0]          # starting from zero
+    assert inc != [1.0, 2.0, 2.0]          # contributions added without transitions
+    rev = orc.scan(M[::-1], U[::-1], np.array([[1.0]]))["final_state"][0, 0]
+    assert rev != g["final_state"]         # order matters
+
+
+def test_scan_single_segment_and_empty():
+    rng = np.random.default_rng(15)
+    M = rng.normal(size=(1, 3, 3))
+    U = rng.normal(size=(1, 3, 2))
+    S = rng.normal(size=(3, 2))
+    r = orc.scan(M, U, S)
+    assert np.array_equal(r["incoming_states"][0], S)
+    assert np.allclose(r["final_state"], M[0] @ S + U[0], rtol=1e-15)
+    assert np.array_equal(r["outgoing_states"][0], r["final_state"])
+    with pytest.raises(ValueError):
+        orc.scan(np.zeros((0, 3, 3)), np.zeros((0, 3, 2)), S)
+
+
+def test_scan_equals_composed_maps_and_exact():
+    rng = np.random.default_rng(16)
+    n, dk, dv = 5, 3, 2
+    M = rng.integers(-4, 5, size=(n, dk, dk)) / 4.0
+    U = rng.integers(-4, 5, size=(n, dk, dv)) / 4.0
+    S = rng.integers(-4, 5, size=(dk, dv)) / 4.0
+    r = orc.scan(M, U, S)
+    # composition rule (M2,U2) o (M1,U1) = (M2 M1, M2 U1 + U2), prefixes applied once
+    Mc, Uc = np.eye(dk), np.zeros((dk, dv))
+    for i in range(n):
+        assert np.allclose(r["incoming_states"][i], Mc @ S + Uc, rtol=1e-13)
+        Mc, Uc = M[i] @ Mc, M[i] @ Uc + U[i]
+        assert np.allclose(r["outgoing_states"][i], Mc @ S + Uc, rtol=1e-13)
+    e = exact.exact_scan(M.tolist(), U.tolist(), S.tolist())
+    assert np.array_equal(np.array(e["final_state"], dtype=float), r["final_state"])
+    assert np.array_equal(np.array(e["incoming_states"], dtype=float), r["incoming_states"])
