@@ -1,0 +1,161 @@
+/*
+ * libkda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention prefill library.
+ *
+ * Every tensor argument is a DEVICE pointer to row-major, contiguous memory
+ * owned by the caller.  Calls validate their host-visible arguments, enqueue
+ * their kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ * return without synchronising.  Nothing is allocated on the device: the
+ * kernels keep every intermediate in registers and LDS.
+ *
+ * Per head the method keeps a state S [dk, dv] (key axis = rows) and for each
+ * token t applies
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * q_t^T S_t,
+ * i.e. decay each key row by its own channel gate, predict k^T S from the
+ * decayed state, delta-write k (beta (v - pred))^T, then read the updated
+ * state (nx_nofloat_kda.nx source: header comment, kda_gate, kda_write,
+ * kda_forward).  The gate is
+ *     log alpha = -exp(a_log[h]) * softplus(raw_gate[t,h,:] + dt_bias[h,:]),
+ * optionally clamped from below ("safe" mode), and beta = sigmoid(beta_logits)
+ * or the logits taken as probabilities (max.nn.state_space.kda_chunk,
+ * Parameters: raw_gate, beta_logits, a_log, dt_bias, gate_mode, beta_mode).
+ * The prefill is evaluated over 64-token chunks with the same result as the
+ * token recurrence (kda_chunk: "same recurrence ... evaluated in parallel
+ * across ... chunks"; its AMD gfx950 pipeline uses 64-token chunks).
+ *
+ * Errors: a status other than KDA_OK is returned BEFORE anything is launched
+ * when a host-checkable argument is wrong (null pointer, extent, dtype, mode,
+ * or a combination outside the supported contract).  Data-dependent
+ * preconditions (cu_seqlens monotone, state_indices in range and distinct)
+ * are not checked by the asynchronous calls; kda_validate_varlen checks them
+ * synchronously.  KDA_ERR_HIP reports a failed kernel launch.
+ */
+#ifndef LIBKDA_H
+#define LIBKDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    KDA_ERR_SHAPE = 2,       /* an extent is negative, zero where it must not be,  */
+                             /* or inconsistent with another                       */
+    KDA_ERR_DTYPE = 3,       /* unknown dtype code                                 */
+    KDA_ERR_UNSUPPORTED = 4, /* valid but outside the supported contract           */
+    KDA_ERR_ARG = 5,         /* bad mode value or scalar                           */
+    KDA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed         */
+    KDA_ERR_DATA = 7         /* kda_validate_varlen: cu_seqlens / indices invalid  */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum { KDA_GATE_ORIGINAL = 0, KDA_GATE_SAFE = 1 } kda_gate_mode;
+typedef enum { KDA_BETA_LOGITS = 0, KDA_BETA_PROBABILITY = 1 } kda_beta_mode;
+typedef enum { KDA_STATE_K_FIRST = 0, KDA_STATE_V_FIRST = 1 } kda_state_layout;
+
+/*
+ * Shapes and modes of one call (max.nn.state_space.kda_chunk, Parameters).
+ * num_heads is both the key-head and value-head count (equal counts only).
+ * Supported contract (anything else -> KDA_ERR_UNSUPPORTED):
+ *   qkv_dtype == out_dtype;
+ *   bf16: dk == dv in {64, 128}, gate_mode SAFE with -5.3 <= gate_lower_bound <= 0
+ *         (the 16-token factorisation of the decay needs 16*|bound| < 85);
+ *   f32:  dk == dv == 64 for kda_chunk_fwd; dk == dv in {64, 128} for
+ *         kda_segment_summary; either gate mode;
+ *   state_layout K_FIRST.
+ */
+typedef struct {
+    int64_t total_tokens;    /* T: rows of q, k, v, raw_gate, beta_logits, out   */
+    int32_t batch;           /* B: sequences (kda_chunk_fwd)                     */
+    int32_t num_heads;       /* H                                                */
+    int32_t dk;              /* key head dim                                     */
+    int32_t dv;              /* value head dim                                   */
+    int32_t max_slots;       /* rows of the state pool (kda_chunk_fwd)           */
+    int32_t qkv_dtype;       /* kda_dtype of q, k, v                             */
+    int32_t out_dtype;       /* kda_dtype of out                                 */
+    int32_t gate_mode;       /* kda_gate_mode                                    */
+    float gate_lower_bound;  /* SAFE mode: log alpha = max(log alpha, bound)     */
+    int32_t beta_mode;       /* kda_beta_mode                                    */
+    int32_t state_layout;    /* kda_state_layout                                 */
+    float scale;             /* o = scale * q^T S (callers usually pass 1/sqrt(dk)) */
+} kda_desc;
+
+/*
+ * Chunk-parallel varlen prefill (max.nn.state_space.kda_chunk).
+ *   q, k        [T, H, dk]   qkv_dtype
+ *   v           [T, H, dv]   qkv_dtype
+ *   raw_gate    [T, H, dk]   f32, forget-gate pre-activation before dt_bias
+ *   beta_logits [T, H]       f32
+ *   a_log       [H]          f32
+ *   dt_bias     [H, dk]      f32
+ *   cu_seqlens  [B+1]        int32, exclusive prefix offsets, cu[0]=0, cu[B]=T
+ *   state_pool  [max_slots, H, dk, dv] f32, K_FIRST; the slot state_indices[b]
+ *               holds sequence b's incoming state and receives its final state.
+ *               No other byte of the pool is read or written.  A sequence of
+ *               length 0 leaves its slot untouched.
+ *   state_indices [B]        int32, distinct slots
+ *   out         [T, H, dv]   out_dtype, every row written; must not alias inputs
+ */
+kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, const void *v,
+                         const float *raw_gate, const float *beta_logits, const float *a_log,
+                         const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
+                         const int32_t *state_indices, void *out, void *stream);
+
+/*
+ * Affine summaries of token segments (KDA Context Parallelism, "Theory": each
+ * segment is the map F_i(S) = M_i S + U_i of its incoming state).  Segment i
+ * covers tokens [seg_offsets[i], seg_offsets[i+1]) of one sequence; for each
+ * head, U_i is the segment's state when started from S = 0 and M_i the
+ * product, later tokens on the left, of (I - beta k k^T) Diag(alpha).
+ *   k [T, H, dk], v [T, H, dv] (qkv_dtype); raw_gate, beta_logits, a_log,
+ *   dt_bias as for kda_chunk_fwd; seg_offsets [n_seg+1] int32 (device),
+ *   monotone with seg_offsets[0] >= 0 and seg_offsets[n_seg] <= T;
+ *   M [n_seg, H, dk, dk] f32, U [n_seg, H, dk, dv] f32 (written).
+ * desc->batch, max_slots, out_dtype and scale are ignored.  n_seg >= 1.
+ */
+kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *v,
+                               const float *raw_gate, const float *beta_logits,
+                               const float *a_log, const float *dt_bias,
+                               const int32_t *seg_offsets, int32_t n_seg, float *M, float *U,
+                               void *stream);
+
+/*
+ * Ordered exclusive prefix of segment maps (KDA Context Parallelism,
+ * "Incoming and outgoing states", "Implementation order"): per head,
+ *   W = S_init[h]; for i = 0..n_seg-1: incoming[i,h] = W; W = M[i,h] W + U[i,h];
+ *   outgoing[i,h] = W;   final_state[h] = W.
+ * Composition (M2,U2) o (M1,U1) = (M2 M1, M2 U1 + U2) is applied in segment
+ * order with the state multiplied on the left.
+ *   M [n_seg, H, dk, dk], U [n_seg, H, dk, dv], S_init [H, dk, dv] (read only);
+ *   incoming, outgoing [n_seg, H, dk, dv], final_state [H, dk, dv] (written).
+ * f32 throughout; dk in {16, 32, ..., 256} (multiple of 16), dv a multiple of 16.
+ * n_seg >= 1 (at least one segment; KDA_ERR_SHAPE otherwise).
+ */
+kda_status kda_affine_exclusive_scan(int32_t n_seg, int32_t num_heads, int32_t dk, int32_t dv,
+                                     const float *M, const float *U, const float *S_init,
+                                     float *incoming, float *outgoing, float *final_state,
+                                     void *stream);
+
+/*
+ * Synchronous debug check of the data-dependent preconditions of
+ * kda_chunk_fwd (max.nn.state_space.kda_chunk, Raises: the shape guards that
+ * a production build leaves out).  cu_seqlens [batch+1] and state_indices
+ * [batch] are DEVICE pointers; returns KDA_ERR_DATA unless cu[0] == 0,
+ * cu is non-decreasing, cu[batch] == total_tokens, and the indices are
+ * distinct and in [0, max_slots).  Blocks until the copies complete.
+ */
+kda_status kda_validate_varlen(const int32_t *cu_seqlens, int32_t batch, int64_t total_tokens,
+                               const int32_t *state_indices, int32_t max_slots);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kda_status_string(kda_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKDA_H */

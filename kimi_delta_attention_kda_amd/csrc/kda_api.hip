@@ -1,0 +1,175 @@
+// kda_api.hip -- C ABI of libkda: argument validation, launch planning, status codes.
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/libkda.h"
+#include "kda_launch.h"
+
+namespace {
+
+bool valid_dtype(int32_t d) { return d == KDA_F32 || d == KDA_BF16; }
+
+// Common host-visible checks of the descriptor for the chunk walk.
+kda_status check_desc(const kda_desc *d, bool summary) {
+    if (!d) return KDA_ERR_NULL;
+    if (d->total_tokens < 0 || d->num_heads <= 0 || d->dk <= 0 || d->dv <= 0) return KDA_ERR_SHAPE;
+    if (d->total_tokens > (int64_t)0x7fffffff) return KDA_ERR_SHAPE;  // int32 offsets
+    if (!summary && (d->batch < 0 || d->max_slots <= 0)) return KDA_ERR_SHAPE;
+    if (!valid_dtype(d->qkv_dtype) || (!summary && !valid_dtype(d->out_dtype))) return KDA_ERR_DTYPE;
+    if (d->gate_mode != KDA_GATE_ORIGINAL && d->gate_mode != KDA_GATE_SAFE) return KDA_ERR_ARG;
+    if (d->beta_mode != KDA_BETA_LOGITS && d->beta_mode != KDA_BETA_PROBABILITY) return KDA_ERR_ARG;
+    if (d->state_layout != KDA_STATE_K_FIRST && d->state_layout != KDA_STATE_V_FIRST) return KDA_ERR_ARG;
+    if (d->gate_mode == KDA_GATE_SAFE && !(d->gate_lower_bound <= 0.f)) return KDA_ERR_ARG;
+    if (!summary && !(d->scale == d->scale)) return KDA_ERR_ARG;  // NaN scale
+    // ---- supported contract
+    if (d->state_layout != KDA_STATE_K_FIRST) return KDA_ERR_UNSUPPORTED;
+    if (d->dk != d->dv) return KDA_ERR_UNSUPPORTED;
+    if (!summary && d->qkv_dtype != d->out_dtype) return KDA_ERR_UNSUPPORTED;
+    if (d->qkv_dtype == KDA_BF16) {
+        if (d->dk != 64 && d->dk != 128) return KDA_ERR_UNSUPPORTED;
+        if (d->gate_mode != KDA_GATE_SAFE) return KDA_ERR_UNSUPPORTED;
+        if (d->gate_lower_bound < -5.3f) return KDA_ERR_UNSUPPORTED;
+    } else {
+        if (summary) {
+            if (d->dk != 64 && d->dk != 128) return KDA_ERR_UNSUPPORTED;
+        } else {
+            if (d->dk != 64) return KDA_ERR_UNSUPPORTED;
+        }
+    }
+    return KDA_OK;
+}
+
+kda::ChainArgs base_args(const kda_desc *d) {
+    kda::ChainArgs a;
+    memset(&a, 0, sizeof(a));
+    a.H = d->num_heads;
+    a.gate_mode = d->gate_mode;
+    a.lb = d->gate_lower_bound;
+    a.beta_mode = d->beta_mode;
+    a.scale = d->scale;
+    return a;
+}
+
+// Value columns per workgroup.  Two 64-column slices per (sequence, head) spread a long
+// sequence over two compute units at the cost of repeating the dv-independent prep.
+int value_slice(int dk, bool precise) {
+    (void)precise;
+    return dk >= 128 ? 64 : 64;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "an extent is out of range or inconsistent";
+        case KDA_ERR_DTYPE: return "unknown dtype code";
+        case KDA_ERR_UNSUPPORTED:
+            return "arguments outside the supported contract (equal heads and dims, dk in {64,128}, "
+                   "K_FIRST, bf16 needs the safe gate with bound >= -5.3, f32 forward needs dk 64)";
+        case KDA_ERR_ARG: return "bad mode value or scalar";
+        case KDA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+        case KDA_ERR_DATA: return "cu_seqlens or state_indices violate their preconditions";
+    }
+    return "unknown status";
+}
+
+kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, const void *v,
+                         const float *raw_gate, const float *beta_logits, const float *a_log,
+                         const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
+                         const int32_t *state_indices, void *out, void *stream) {
+    kda_status st = check_desc(desc, false);
+    if (st != KDA_OK) return st;
+    if (!a_log || !dt_bias || !cu_seqlens || !state_pool || (desc->batch > 0 && !state_indices))
+        return KDA_ERR_NULL;
+    if (desc->total_tokens > 0 && (!q || !k || !v || !raw_gate || !beta_logits || !out)) return KDA_ERR_NULL;
+    if (desc->batch == 0 || desc->total_tokens == 0) {
+        // no tokens: nothing to read or write (every sequence is empty)
+        return KDA_OK;
+    }
+    const bool precise = desc->qkv_dtype == KDA_F32;
+    kda::ChainArgs a = base_args(desc);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.raw_gate = raw_gate;
+    a.beta_logits = beta_logits;
+    a.a_log = a_log;
+    a.dt_bias = dt_bias;
+    a.offsets = cu_seqlens;
+    a.state_pool = state_pool;
+    a.state_indices = state_indices;
+    a.out = out;
+    a.n_items = desc->batch;
+    const int dvs = value_slice(desc->dk, precise);
+    a.n_slices = desc->dv / dvs;
+    hipError_t e = kda::launch_chain(a, desc->dk, dvs, precise, kda::MODE_FWD, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *v,
+                               const float *raw_gate, const float *beta_logits,
+                               const float *a_log, const float *dt_bias,
+                               const int32_t *seg_offsets, int32_t n_seg, float *M, float *U,
+                               void *stream) {
+    kda_status st = check_desc(desc, true);
+    if (st != KDA_OK) return st;
+    if (n_seg < 1) return KDA_ERR_SHAPE;
+    if (!a_log || !dt_bias || !seg_offsets || !M || !U) return KDA_ERR_NULL;
+    if (desc->total_tokens > 0 && (!k || !v || !raw_gate || !beta_logits)) return KDA_ERR_NULL;
+    const bool precise = desc->qkv_dtype == KDA_F32;
+    kda::ChainArgs a = base_args(desc);
+    a.k = k;
+    a.v = v;
+    a.raw_gate = raw_gate;
+    a.beta_logits = beta_logits;
+    a.a_log = a_log;
+    a.dt_bias = dt_bias;
+    a.offsets = seg_offsets;
+    a.M = M;
+    a.U = U;
+    a.n_items = n_seg;
+    const int dvs = value_slice(desc->dk, precise);
+    a.n_slices = (desc->dk + desc->dv) / dvs;
+    hipError_t e = kda::launch_chain(a, desc->dk, dvs, precise, kda::MODE_SUMMARY, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_affine_exclusive_scan(int32_t n_seg, int32_t num_heads, int32_t dk, int32_t dv,
+                                     const float *M, const float *U, const float *S_init,
+                                     float *incoming, float *outgoing, float *final_state,
+                                     void *stream) {
+    if (n_seg < 1 || num_heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_SHAPE;
+    if (!M || !U || !S_init || !incoming || !outgoing || !final_state) return KDA_ERR_NULL;
+    if (!(dk == 16 || dk == 32 || dk == 64 || dk == 128) || dv % 16 != 0) return KDA_ERR_UNSUPPORTED;
+    hipError_t e = kda::launch_affine_scan(n_seg, num_heads, dk, dv, M, U, S_init, incoming, outgoing,
+                                           final_state, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_validate_varlen(const int32_t *cu_seqlens, int32_t batch, int64_t total_tokens,
+                               const int32_t *state_indices, int32_t max_slots) {
+    if (batch < 0 || total_tokens < 0 || max_slots <= 0) return KDA_ERR_SHAPE;
+    if (!cu_seqlens || (batch > 0 && !state_indices)) return KDA_ERR_NULL;
+    std::vector<int32_t> cu(batch + 1), idx(batch > 0 ? batch : 1);
+    if (hipMemcpy(cu.data(), cu_seqlens, sizeof(int32_t) * (batch + 1), hipMemcpyDeviceToHost) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (batch > 0 &&
+        hipMemcpy(idx.data(), state_indices, sizeof(int32_t) * batch, hipMemcpyDeviceToHost) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (cu[0] != 0 || (int64_t)cu[batch] != total_tokens) return KDA_ERR_DATA;
+    for (int b = 0; b < batch; ++b)
+        if (cu[b + 1] < cu[b]) return KDA_ERR_DATA;
+    std::vector<char> seen(max_slots, 0);
+    for (int b = 0; b < batch; ++b) {
+        if (idx[b] < 0 || idx[b] >= max_slots || seen[idx[b]]) return KDA_ERR_DATA;
+        seen[idx[b]] = 1;
+    }
+    return KDA_OK;
+}
+
+}  // extern "C"
