@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Throughput of the KDA chunk-parallel prefill (kda_chunk_fwd) on one MI355X.
+
+One step = one kda_chunk_fwd call over the whole varlen batch (gate prep, decayed
+scores, triangular inverse, W/U construction, inter-chunk state pass, output): the
+entire hot path runs inside one kernel launch.  Inputs are seeded synthetic tensors
+already resident in HBM.  Prints one JSON line.
+
+Default workload: 8 sequences (lengths uniform in [1024, 8192], 32768 tokens), H=32,
+dk=dv=128, bf16 q/k/v/out, fp32 gates and state, safe gate (bound -5), 64-slot pool.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s at H=32 dk=dv=128 bf16, 32K tokens; % MFMA peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_varlen_32k_traffic.json")
+
+
+def kernel_source_sha() -> str:
+    d = os.path.join(ROOT, "kimi_delta_attention_kda_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w) -> int:
+    """Compulsory HBM bytes of one call: every input read once, out written once,
+    each used pool slot read and written once."""
+    e_qkv = 2 if w.dtype == "bf16" else 4
+    per_token_head = 2 * w.dk * e_qkv + w.dv * e_qkv + w.dv * e_qkv + w.dk * 4 + 4
+    pool = 2 * w.B * w.H * w.dk * w.dv * 4
+    return w.T * w.H * per_token_head + pool + w.H * (w.dk + 1) * 4 + (w.B + 1) * 4 + w.B * 4
+
+
+def algorithmic_flops(w) -> int:
+    """Triangle-aware chunk-form flops: C(3dk + 2dv) + 6 dk dv per token-head (C = 64)."""
+    return w.T * w.H * (64 * (3 * w.dk + 2 * w.dv) + 6 * w.dk * w.dv)
+
+
+def dense_tile_flops(w) -> int:
+    return w.T * w.H * (2 * 64 * (3 * w.dk + 2 * w.dv) + 6 * w.dk * w.dv)
+
+
+def cpu_baseline(w, inp, target_s=12.0):
+    """The fp64 oracle on a bounded sample of the same workload, all host cores."""
+    from oracle import build as obuild
+    from oracle import oracle as orc
+    obuild.build(force=False)
+    nth = orc.default_threads()
+    # calibrate on one short item
+    b0 = min(range(w.B), key=lambda b: w.lengths[b])
+    t = time.perf_counter()
+    orc.forward_items([orc.item_from_inputs(inp, b0, 0)], w.dk, w.dv, w.gate_mode, w.lower_bound,
+                      w.beta_mode, w.scale, nthreads=1)
+    per_tok = (time.perf_counter() - t) / max(1, w.lengths[b0])
+    # pick heads so the sample is about target_s of wall time on nth threads
+    heads = max(1, min(w.H, int(target_s * nth / (per_tok * w.T))))
+    items = [(b, h) for h in range(heads) for b in range(w.B)]
+    its = [orc.item_from_inputs(inp, b, h) for (b, h) in items]
+    t = time.perf_counter()
+    orc.forward_items(its, w.dk, w.dv, w.gate_mode, w.lower_bound, w.beta_mode, w.scale, nthreads=nth)
+    dt = time.perf_counter() - t
+    token_heads = sum(w.lengths[b] for (b, _) in items)
+    return {"value": token_heads / w.H / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+            "sample": f"all {w.B} sequences x heads 0..{heads - 1} of {w.H} "
+                      f"({token_heads} token-heads, {dt:.1f} s), scaled to all heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="varlen_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by heads or sequences with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kimi_delta_attention_kda_amd as kda
+    from kimi_delta_attention_kda_amd import workloads as wl
+
+    w = wl.workload(args.workload)
+    if w.segments:
+        raise SystemExit("bench.py times kda_chunk_fwd workloads")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload={w.name} T={w.T} B={w.B} H={w.H} dk={w.dk} dv={w.dv} dtype={w.dtype}",
+          file=sys.stderr, flush=True)
+    inp = wl.make_inputs(w, dev)
+    torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, inp)
+        print(f"[bench] cpu_baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} threads",
+              file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: 3 x 1 GiB read + 1 GiB write", file=sys.stderr, flush=True)
+        del src, dst
+
+    pool = inp["state_pool"]
+    gate = "safe" if w.gate_mode == 1 else "original"
+
+    def step(out):
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["raw_gate"], inp["beta_logits"], inp["a_log"],
+                      inp["dt_bias"], inp["cu_seqlens"], pool, inp["state_indices"], gate_mode=gate,
+                      lower_bound=w.lower_bound, scale=w.scale, out=out)
+
+    out = torch.empty((w.T, w.H, w.dv), dtype=inp["q"].dtype, device=dev)
+    for _ in range(args.warmup):
+        step(out)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(out)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    tokens_s = w.T / (ms_step / 1e3)
+
+    nbytes = algorithmic_bytes(w)
+    achieved = nbytes / (kern_ms / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha") == kernel_source_sha() and tr.get("workload") == w.name:
+            traffic = tr.get("hbm_bytes_per_launch")
+    fl = algorithmic_flops(w)
+    fl_dense = dense_tile_flops(w)
+    rec = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "total_tokens": w.T, "sequences": w.B, "lengths": list(w.lengths),
+                   "heads": w.H, "dk": w.dk, "dv": w.dv, "chunk": 64,
+                   "gate": gate, "gate_lower_bound": w.lower_bound, "pool_slots": w.n_slots},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "kda_chain_kernel", "kernel_ms": round(kern_ms, 4),
+                     "algorithmic_bytes_per_launch": nbytes},
+        "mfma": {"algorithmic_tflops": round(fl / (kern_ms / 1e3) / 1e12, 2),
+                 "frac_of_bf16_peak": round(fl / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "dense_tile_frac_of_bf16_peak": round(fl_dense / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "flops_per_launch_algorithmic": fl},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

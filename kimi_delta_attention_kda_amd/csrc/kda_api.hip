@@ -51,12 +51,14 @@ kda::ChainArgs base_args(const kda_desc *d) {
     return a;
 }
 
-// Value columns per workgroup.  Two 64-column slices per (sequence, head) spread a long
-// sequence over two compute units at the cost of repeating the dv-independent prep.
+// Value columns per workgroup of the general chunk walk (kda_chain.hip).
 int value_slice(int dk, bool precise) {
+    (void)dk;
     (void)precise;
-    return dk >= 128 ? 64 : 64;
+    return 64;
 }
+
+bool use_fast(const kda_desc *d) { return d->qkv_dtype == KDA_BF16 && d->dk == 128 && d->dv == 128; }
 
 }  // namespace
 
@@ -105,9 +107,15 @@ kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, con
     a.state_indices = state_indices;
     a.out = out;
     a.n_items = desc->batch;
-    const int dvs = value_slice(desc->dk, precise);
-    a.n_slices = desc->dv / dvs;
-    hipError_t e = kda::launch_chain(a, desc->dk, dvs, precise, kda::MODE_FWD, (hipStream_t)stream);
+    hipError_t e;
+    if (use_fast(desc)) {
+        a.n_slices = 1;
+        e = kda::launch_fast(a, kda::MODE_FWD, (hipStream_t)stream);
+    } else {
+        const int dvs = value_slice(desc->dk, precise);
+        a.n_slices = desc->dv / dvs;
+        e = kda::launch_chain(a, desc->dk, dvs, precise, kda::MODE_FWD, (hipStream_t)stream);
+    }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -133,9 +141,15 @@ kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *
     a.M = M;
     a.U = U;
     a.n_items = n_seg;
-    const int dvs = value_slice(desc->dk, precise);
-    a.n_slices = (desc->dk + desc->dv) / dvs;
-    hipError_t e = kda::launch_chain(a, desc->dk, dvs, precise, kda::MODE_SUMMARY, (hipStream_t)stream);
+    hipError_t e;
+    if (use_fast(desc)) {
+        a.n_slices = 2;
+        e = kda::launch_fast(a, kda::MODE_SUMMARY, (hipStream_t)stream);
+    } else {
+        const int dvs = value_slice(desc->dk, precise);
+        a.n_slices = (desc->dk + desc->dv) / dvs;
+        e = kda::launch_chain(a, desc->dk, dvs, precise, kda::MODE_SUMMARY, (hipStream_t)stream);
+    }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

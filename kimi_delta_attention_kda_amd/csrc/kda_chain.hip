@@ -260,9 +260,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 
         // beta of the chunk rows (0 beyond the sequence end)
         if (t < 64) {
-            float bv = 0.f;
-            if (t < n) bv = beta_of(a.beta_logits[(int64_t)(t0 + t) * H + h], a.beta_mode);
-            sBeta[t] = bv;
+            const float x = a.beta_logits[(int64_t)(t0 + min(t, n - 1)) * H + h];
+            sBeta[t] = (t < n) ? beta_of(x, a.beta_mode) : 0.f;
         }
 
         if constexpr (!PRECISE) {
@@ -282,26 +281,38 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 
             const int I = w;        // 16-row block owned by this wave in the prep
             const int c0 = l * CPT;
+            // Issue every global load of the chunk before any use: rows past the end
+            // read the last valid row (always in bounds) and are masked afterwards.
+            float rg[16][CPT];
+            bf16_t kr[16][CPT], qr[16][CPT], vr[NVT][16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ic = min(16 * I + r, n - 1);
+                const int64_t base = ((int64_t)(t0 + ic) * H + h) * DK + c0;
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    rg[r][cc] = a.raw_gate[base + cc];
+                    kr[r][cc] = kb16[base + cc];
+                    if (FW) qr[r][cc] = qb16[base + cc];
+                }
+                if (has_v) {
+                    const int64_t vb = ((int64_t)(t0 + ic) * H + h) * DV + col0 + l;
+#pragma unroll
+                    for (int m = 0; m < NVT; ++m) vr[m][r] = vb16[vb + 64 * m];
+                }
+            }
             float al[16][CPT], kf[16][CPT], qf[16][CPT];
             float dtb[CPT];
 #pragma unroll
             for (int cc = 0; cc < CPT; ++cc) dtb[cc] = a.dt_bias[h * DK + c0 + cc];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int i = 16 * I + r;
-                const bool valid = i < n;
-                const int64_t base = ((int64_t)(t0 + i) * H + h) * DK + c0;
+                const bool valid = 16 * I + r < n;
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
-                    float rg = 0.f, kk = 0.f, qq = 0.f;
-                    if (valid) {
-                        rg = a.raw_gate[base + cc];
-                        kk = (float)kb16[base + cc];
-                        if (FW) qq = (float)qb16[base + cc];
-                    }
-                    al[r][cc] = valid ? __expf(gate_log_alpha(rg, dtb[cc], Ah, safe, lb)) : 1.f;
-                    kf[r][cc] = kk;
-                    qf[r][cc] = qq;
+                    al[r][cc] = valid ? __expf(gate_log_alpha(rg[r][cc], dtb[cc], Ah, safe, lb)) : 1.f;
+                    kf[r][cc] = valid ? (float)kr[r][cc] : 0.f;
+                    qf[r][cc] = (FW && valid) ? (float)qr[r][cc] : 0.f;
                 }
             }
             // value slice, transposed: sVT[v][row]
@@ -311,9 +322,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 bf16x8 lo8, hi8;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int i = 16 * I + r;
-                    bf16_t x = (bf16_t)0.f;
-                    if (has_v && i < n) x = vb16[((int64_t)(t0 + i) * H + h) * DV + col0 + vv];
+                    const bf16_t x = (has_v && 16 * I + r < n) ? vr[m][r] : (bf16_t)0.f;
                     if (r < 8) lo8[r] = x; else hi8[r - 8] = x;
                 }
                 *(bf16x8 *)(sVT + vv * PJ + 16 * I) = lo8;
@@ -549,13 +558,10 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int i = i0 + r;
-                        const int64_t base = ((int64_t)(t0 + i) * H + h) * DK + c;
-                        rg[r] = 0.f; kk[r] = 0.f; qq[r] = 0.f;
-                        if (i < n) {
-                            rg[r] = a.raw_gate[base];
-                            kk[r] = kf32[base];
-                            if (FW) qq[r] = qf32[base];
-                        }
+                        const int64_t base = ((int64_t)(t0 + min(i, n - 1)) * H + h) * DK + c;
+                        rg[r] = a.raw_gate[base];
+                        kk[r] = i < n ? kf32[base] : 0.f;
+                        qq[r] = (FW && i < n) ? qf32[base] : 0.f;
                     }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -571,12 +577,16 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 #pragma unroll
             for (int m = 0; m < NVT; ++m) {
                 const int vv = l + 64 * m;
+                float xv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int i = 16 * w + r;
-                    float x = 0.f;
-                    if (has_v && i < n) x = vf32[((int64_t)(t0 + i) * H + h) * DV + col0 + vv];
-                    sVT[vv * PF + i] = x;
+                    xv[r] = has_v ? vf32[((int64_t)(t0 + min(i, n - 1)) * H + h) * DV + col0 + vv] : 0.f;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = 16 * w + r;
+                    sVT[vv * PF + i] = (i < n) ? xv[r] : 0.f;
                 }
             }
             __syncthreads();

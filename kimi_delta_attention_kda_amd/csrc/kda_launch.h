@@ -34,6 +34,11 @@ struct ChainArgs {
 // dvs: value columns per workgroup (64 or 128); precise: fp32 inputs.
 hipError_t launch_chain(const ChainArgs &a, int dk, int dvs, bool precise, int mode, hipStream_t stream);
 
+// bf16 inputs, dk = dv = 128, safe gate: 8-wave kernel, one workgroup per (item, head)
+// for the forward pass (n_slices = 1) and two (transition / contribution columns) for
+// segment summaries (n_slices = 2).
+hipError_t launch_fast(const ChainArgs &a, int mode, hipStream_t stream);
+
 hipError_t launch_affine_scan(int n_seg, int H, int dk, int dv, const float *M, const float *U,
                               const float *S_init, float *incoming, float *outgoing, float *final_state,
                               hipStream_t stream);

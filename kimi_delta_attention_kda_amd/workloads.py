@@ -26,7 +26,7 @@ Each named workload fixes shapes, dtypes, gate mode and sequence-length mix:
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field, replace
+from dataclasses import dataclass
 
 import numpy as np
 import torch
@@ -49,7 +49,9 @@ class Workload:
     canary_unused: bool = True
     seed: int = 0
     segments: int = 0         # >0: segment-summary workload, equal segments
-    extra: dict = field(default_factory=dict)
+    raw_mean: float = 0.0     # raw_gate ~ N(raw_mean, 1)
+    beta_mean: float = 0.0    # beta_logits ~ N(beta_mean, beta_sigma^2)
+    a_log_hi: float = math.log(16.0)  # a_log ~ U(0, a_log_hi)
 
     @property
     def T(self) -> int:
@@ -105,6 +107,14 @@ def custom(lengths, H=2, dk=64, dv=64, dtype="bf16", gate_mode=1, n_slots=None,
                     state_sigma=state_sigma, beta_sigma=beta_sigma, seed=seed, **kw)
 
 
+def slow_gate_segments(segments=4, seg_len=2048, H=2, dk=128, seed=0) -> Workload:
+    """Segment workload whose maps stay O(1): log-alpha ~ -1e-5 (a_log = 0,
+    raw_gate ~ N(-11.5, 1)) and beta ~ 1e-3 (beta_logits ~ N(-7, 1))."""
+    return Workload("slow_gate_segments", (segments * seg_len,), H, dk, dk, "f32", 0, n_slots=1,
+                    state_sigma=0.01, segments=segments, raw_mean=-11.5, beta_mean=-7.0,
+                    a_log_hi=0.0, seed=seed)
+
+
 def torch_dtype(d: str):
     return {"f32": torch.float32, "bf16": torch.bfloat16}[d]
 
@@ -133,9 +143,9 @@ def make_inputs(w: Workload, device="cpu") -> dict:
     q = unit_rows(normal(T, H, dk)).to(dt)
     k = unit_rows(normal(T, H, dk)).to(dt)
     v = normal(T, H, dv).to(dt)
-    raw_gate = normal(T, H, dk)
-    beta_logits = normal(T, H, std=w.beta_sigma)
-    a_log = torch.rand(H, generator=g, device=device, dtype=torch.float32) * math.log(16.0)
+    raw_gate = normal(T, H, dk) + w.raw_mean
+    beta_logits = normal(T, H, std=w.beta_sigma) + w.beta_mean
+    a_log = torch.rand(H, generator=g, device=device, dtype=torch.float32) * w.a_log_hi
     dt_bias = normal(H, dk, std=0.1)
 
     cu = np.zeros(w.B + 1, dtype=np.int64)

@@ -1,0 +1,136 @@
+"""CPU-side checks of the C ABI: exported symbols, status strings, and every
+host-checkable error path (validation returns before any device work, so these
+run without a GPU).  Also: the binding fails loudly when the library is missing."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import kimi_delta_attention_kda_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libkda.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EARG = 0, 1, 2, 3, 4, 5
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kda.LIB_PATH):
+        from kimi_delta_attention_kda_amd import build
+        build.build()
+    return kda.lib()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kda_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_function_is_exported(L):
+    names = _declared_functions()
+    assert {"kda_chunk_fwd", "kda_segment_summary", "kda_affine_exclusive_scan",
+            "kda_validate_varlen", "kda_status_string"} <= set(names)
+    nm = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (kda_\w+)$", nm, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_status_strings(L):
+    for code in range(8):
+        s = kda.status_string(code)
+        assert isinstance(s, str) and s
+    assert kda.status_string(0) == "ok"
+    assert kda.status_string(99) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(T=128, B=2, H=4, dk=128, dv=128, max_slots=4, qkv_dtype=torch.bfloat16,
+                out_dtype=torch.bfloat16, gate_mode="safe", lower_bound=-5.0)
+    base.update(kw)
+    return kda.make_desc(base["T"], base["B"], base["H"], base["dk"], base["dv"], base["max_slots"],
+                         base["qkv_dtype"], base["out_dtype"], base["gate_mode"], base["lower_bound"])
+
+
+def _fwd(L, d, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, raw=FAKE, beta=FAKE, a_log=FAKE, dtb=FAKE, cu=FAKE, pool=FAKE,
+             idx=FAKE, out=FAKE)
+    p.update(ptrs)
+    return L.kda_chunk_fwd(C.byref(d) if d is not None else None, p["q"], p["k"], p["v"], p["raw"],
+                           p["beta"], p["a_log"], p["dtb"], p["cu"], p["pool"], p["idx"], p["out"], None)
+
+
+def test_chunk_fwd_error_paths(L):
+    assert _fwd(L, None) == ENULL
+    assert _fwd(L, _desc(), q=None) == ENULL
+    assert _fwd(L, _desc(), pool=None) == ENULL
+    assert _fwd(L, _desc(), cu=None) == ENULL
+    assert _fwd(L, _desc(T=-1)) == ESHAPE
+    assert _fwd(L, _desc(H=0)) == ESHAPE
+    assert _fwd(L, _desc(max_slots=0)) == ESHAPE
+    assert _fwd(L, _desc(qkv_dtype=torch.float16)) == EDTYPE
+    assert _fwd(L, _desc(gate_mode="original")) == EUNSUP          # bf16 needs the safe gate
+    assert _fwd(L, _desc(lower_bound=-6.0)) == EUNSUP               # 16*|bound| must stay < 85
+    assert _fwd(L, _desc(lower_bound=0.5)) == EARG
+    assert _fwd(L, _desc(dk=128, dv=64)) == EUNSUP
+    assert _fwd(L, _desc(dk=96, dv=96)) == EUNSUP
+    assert _fwd(L, _desc(out_dtype=torch.float32)) == EUNSUP
+    assert _fwd(L, _desc(qkv_dtype=torch.float32, out_dtype=torch.float32)) == EUNSUP  # f32 fwd: dk 64
+    d = _desc()
+    d.state_layout = 1
+    assert _fwd(L, d) == EUNSUP                                     # V_FIRST
+    d = _desc()
+    d.gate_mode = 7
+    assert _fwd(L, d) == EARG
+    d = _desc()
+    d.beta_mode = 3
+    assert _fwd(L, d) == EARG
+    # nothing to do: no sequences / no tokens (returns before any launch)
+    assert _fwd(L, _desc(B=0)) == OK
+    assert _fwd(L, _desc(T=0)) == OK
+
+
+def test_summary_and_scan_error_paths(L):
+    d = _desc()
+    args = [FAKE] * 7
+    assert L.kda_segment_summary(C.byref(d), *args, 0, FAKE, FAKE, None) == ESHAPE    # n_seg >= 1
+    assert L.kda_segment_summary(C.byref(d), *args, 2, None, FAKE, None) == ENULL
+    d32 = _desc(qkv_dtype=torch.float32, dk=96, dv=96)
+    assert L.kda_segment_summary(C.byref(d32), *args, 2, FAKE, FAKE, None) == EUNSUP
+    sargs = [FAKE] * 6
+    assert L.kda_affine_exclusive_scan(0, 2, 16, 16, *sargs, None) == ESHAPE           # n_seg >= 1
+    assert L.kda_affine_exclusive_scan(2, 2, 48, 16, *sargs, None) == EUNSUP
+    assert L.kda_affine_exclusive_scan(2, 2, 16, 8, *sargs, None) == EUNSUP
+    assert L.kda_affine_exclusive_scan(2, 2, 16, 16, None, *sargs[1:], None) == ENULL
+    assert L.kda_validate_varlen(FAKE, -1, 0, FAKE, 4) == ESHAPE
+    assert L.kda_validate_varlen(None, 2, 0, FAKE, 4) == ENULL
+
+
+def test_python_binding_checks_before_the_library():
+    T, H, dk = 8, 2, 64
+    q = torch.zeros(T, H, dk, dtype=torch.bfloat16)
+    raw = torch.zeros(T, H, dk)
+    with pytest.raises(ValueError):   # k has the wrong extent
+        kda.chunk_fwd(q, torch.zeros(T, H, 32, dtype=torch.bfloat16), q, raw, torch.zeros(T, H),
+                      torch.zeros(H), torch.zeros(H, dk), torch.tensor([0, T], dtype=torch.int32),
+                      torch.zeros(1, H, dk, dk), torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError):   # wrong dtype of the gate
+        kda.chunk_fwd(q, q, q, raw.double(), torch.zeros(T, H), torch.zeros(H), torch.zeros(H, dk),
+                      torch.tensor([0, T], dtype=torch.int32), torch.zeros(1, H, dk, dk),
+                      torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError):   # at least one segment
+        kda.context_parallel(torch.zeros(0, 16, 16), torch.zeros(0, 16, 16), torch.zeros(16, 16))
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(kda, "_lib", None)
+    monkeypatch.setattr(kda, "LIB_PATH", "/nonexistent/libkda.so")
+    with pytest.raises(RuntimeError):
+        kda.lib()
