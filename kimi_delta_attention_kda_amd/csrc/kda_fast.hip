@@ -8,15 +8,19 @@
 //    the dv-independent work of a chunk (gate, decay factors, scores, inverses) is done
 //    once; each wave owns one 16-column tile of the fp32 state (128 x 16, in MFMA
 //    accumulators) for the whole sequence;
-//  * the gate is computed by one thread per (16-row block, key channel); decay factors
-//    are running products of alpha along the block (no exp of differences at all);
+//  * prep threads own 4 adjacent key channels x 4 rows of one 16-row block: the gate
+//    pre-activations arrive as 16-byte loads, k/q/v as 8-byte loads, operand rows leave
+//    as 8-byte LDS stores; decay factors are running products of alpha (no exp of
+//    differences), completed across the four quarter blocks with quad lane broadcasts;
 //  * decayed scores come from bf16 MFMAs on 16x16 blocks whose operands carry factors
-//    <= 1, plus one precomputed per-channel factor per block pair (see kda_chain.hip);
-//  * the unit lower-triangular system (I + A) U = R is solved per wave by blocked
-//    forward substitution: 16x16 diagonal-block inverses (fp32 substitution, once per
-//    chunk) and 16x16x16 bf16 MFMAs with the right-hand side split hi+lo;
-//  * global loads of chunk c+1 are issued before the scores of chunk c are built, so
-//    their latency hides behind the chunk's compute.
+//    <= 1, times one per-channel factor per block pair (see kda_chain.hip);
+//  * (I + A) U = R is solved per wave by blocked forward substitution with fp16
+//    16x16x16 MFMAs: 16x16 diagonal-block inverses (fp32 right-looking substitution,
+//    once per chunk) and the right-hand side split into fp16 hi + lo;
+//  * the state update uses fp16 Khat (|Khat| <= 1) against fp16 hi + lo U; products
+//    with the state itself (Kg S, Qbar S) are bf16, whose range matches fp32;
+//  * global loads of chunk c+1 are issued before the scores of chunk c are built and
+//    land in plain 32-bit registers, so nothing waits on them until chunk c+1.
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -27,47 +31,91 @@ namespace fast {
 constexpr int NT = 512;  // 8 waves
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int PK = DK + 8;  // bf16 pitch of [64][DK] arrays
-constexpr int PJ = 64 + 8;  // bf16 pitch of [*][64] arrays
+constexpr int PK = DK + 8;  // 16-bit element pitch of [64][DK] arrays
+constexpr int PJ = 64 + 8;  // 16-bit element pitch of [*][64] arrays
+
+typedef _Float16 f16_t;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 template <int MODE>
 struct Lds {
     static constexpr bool FW = MODE == MODE_FWD;
-    static constexpr int KR = 0;                          // Kr, then Kg           bf16 [64][PK]
-    static constexpr int QR = KR + 64 * PK * 2;           // Qr, then Qbar (FWD)   bf16 [64][PK]
-    static constexpr int KC = QR + (FW ? 64 * PK * 2 : 0);// Kc                   bf16 [64][PK]
-    static constexpr int KHH = KC + 64 * PK * 2;          // Khat^T hi            bf16 [DK][PJ]
-    static constexpr int KHL = KHH + DK * PJ * 2;         // Khat^T lo
-    static constexpr int VT = KHL + DK * PJ * 2;          // V^T                   bf16 [DV][PJ]
-    static constexpr int AO = VT + DV * PJ * 2;           // -A, off-diagonal blocks bf16 [64][PJ]
-    static constexpr int P = AO + 64 * PJ * 2;            // P (FWD)               bf16 [64][PJ]
-    static constexpr int AD = P + (FW ? 64 * PJ * 2 : 0); // A, diagonal blocks    f32 [4][16][17]
-    static constexpr int D = AD + 4 * 16 * 17 * 4;        // (I + A_II)^-1         bf16 [4][16][24]
+    static constexpr int ROWS = 64 * PK * 2;              // one [64][PK] 16-bit array
+    static constexpr int KR = 0;                          // Kr            bf16, scores
+    static constexpr int QR = KR + ROWS;                  // Qr (FWD)      bf16, scores
+    static constexpr int KC = QR + (FW ? ROWS : 0);       // Kc            bf16, scores
+    static constexpr int KG = KC + ROWS;                  // Kg            bf16, chain
+    static constexpr int QB = KG + ROWS;                  // Qbar (FWD)    bf16, chain
+    static constexpr int KH = QB + (FW ? ROWS : 0);       // Khat^T        f16 [DK][PJ]
+    static constexpr int VT = KH + DK * PJ * 2;           // V^T           bf16 [DV][PJ]
+    static constexpr int AO = VT + DV * PJ * 2;           // -A off-diag   f16 [64][PJ]
+    static constexpr int P = AO + 64 * PJ * 2;            // P (FWD)       f16 [64][PJ]
+    static constexpr int AD = P + (FW ? 64 * PJ * 2 : 0); // A diag blocks f32 [4][16][20]
+    static constexpr int D = AD + 4 * 16 * 20 * 4;        // (I+A_II)^-1   f16 [4][16][24]
     static constexpr int BETA = D + 4 * 16 * 24 * 2;      // f32 [64]
-    static constexpr int E = BETA + 64 * 4;               // block decays          f32 [4][DK]
-    static constexpr int MF = E + 4 * DK * 4;             // pair factors          f32 [10][DK]
-    static constexpr int EG = MF + 10 * DK * 4;           // e^{G_last}            f32 [DK]
+    static constexpr int E = BETA + 64 * 4;               // block decays  f32 [4][DK]
+    static constexpr int IE = E + 4 * DK * 4;             // 1/decays      f32 [4][DK]
+    static constexpr int EG = IE + 4 * DK * 4;            // e^{G_last}    f32 [DK]
     static constexpr int BYTES = EG + DK * 4;
 };
 
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma16h(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma32h(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 cath(f16x4 a, f16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// A-operand fragment whose k slots follow the accumulator row order of two 16-row
+// tiles: slot s<4 -> column k0+4g+s, slot s>=4 -> column k0+16+4g+(s-4).
 __device__ __forceinline__ bf16x8 fragA_perm(const bf16_t *base, int pitch, int row, int k0, int g) {
     const bf16_t *p = base + row * pitch + k0 + 4 * g;
     return cat(*(const bf16x4 *)p, *(const bf16x4 *)(p + 16));
 }
-
-__device__ __forceinline__ float gate_alpha(float raw, float dtb, float Ah, int safe, float lb) {
-    float la = -Ah * softplus_f(raw + dtb);
-    if (safe) la = fmaxf(la, lb);
-    return __expf(la);
+__device__ __forceinline__ f16x8 fragA_perm_h(const f16_t *base, int pitch, int row, int k0, int g) {
+    const f16_t *p = base + row * pitch + k0 + 4 * g;
+    return cath(*(const f16x4 *)p, *(const f16x4 *)(p + 16));
 }
 
-// block pairs (I, J<=I): diagonal pairs 0..3, then the off-diagonal ones
-__device__ __constant__ int kPairI[10] = {0, 1, 2, 3, 1, 2, 2, 3, 3, 3};
-__device__ __constant__ int kPairJ[10] = {0, 1, 2, 3, 0, 0, 1, 0, 1, 2};
+__device__ __forceinline__ void split_h(f32x4 x, f16x4 &hi, f16x4 &lo) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        hi[s] = (f16_t)x[s];
+        lo[s] = (f16_t)(x[s] - (float)hi[s]);
+    }
+}
+
+// alpha = exp(-A softplus(x)) = (1 + e^x)^(-A), computed as 2^(-A log2(1 + 2^(x log2 e)));
+// the safe gate's floor on log alpha is a floor exp(bound) on alpha.  Branch-free: the
+// three transcendentals are the hardware base-2 exp/log.
+__device__ __forceinline__ float gate_alpha(float raw, float dtb, float negA, float amin) {
+    const float t = __builtin_amdgcn_exp2f((raw + dtb) * 1.44269504088896341f);
+    const float a = __builtin_amdgcn_exp2f(negA * __builtin_amdgcn_logf(1.f + t));
+    return fmaxf(a, amin);
+}
+
+// value held by lane q of this lane's quad (DPP quad permutation [q, q, q, q])
+template <int Q>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), Q * 0x55, 0xF, 0xF, false));
+}
+
+// Block pairs (I, J <= I) of the 4x4 grid of 16x16 score blocks handled by wave w in the
+// score phase: waves 0-3 take the diagonal pair (w, w); waves 4..7 take the off-diagonal
+// pairs {(1,0),(2,1)}, {(2,0),(3,2)}, {(3,0)}, {(3,1)}.  Arithmetic, so that no memory
+// access (and no wait on the in-flight prefetch) is needed to find them.
+__device__ __forceinline__ int n_pairs_of_wave(int w) { return (w == 4 || w == 5) ? 2 : 1; }
+__device__ __forceinline__ void pair_of_wave(int w, int pp, int &bI, int &bJ) {
+    if (w < 4) { bI = w; bJ = w; return; }
+    if (w == 4) { bI = 1 + pp; bJ = pp; return; }
+    if (w == 5) { bI = 2 + pp; bJ = 2 * pp; return; }
+    bI = 3;
+    bJ = w - 6;
+}
 
 template <int MODE>
 __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
@@ -77,16 +125,17 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     bf16_t *sKR = (bf16_t *)(smem + L::KR);
     bf16_t *sQR = (bf16_t *)(smem + L::QR);
     bf16_t *sKC = (bf16_t *)(smem + L::KC);
-    bf16_t *sKHH = (bf16_t *)(smem + L::KHH);
-    bf16_t *sKHL = (bf16_t *)(smem + L::KHL);
+    bf16_t *sKG = (bf16_t *)(smem + L::KG);
+    bf16_t *sQB = (bf16_t *)(smem + L::QB);
+    f16_t *sKH = (f16_t *)(smem + L::KH);
     bf16_t *sVT = (bf16_t *)(smem + L::VT);
-    bf16_t *sAO = (bf16_t *)(smem + L::AO);
-    bf16_t *sP = (bf16_t *)(smem + L::P);
+    f16_t *sAO = (f16_t *)(smem + L::AO);
+    f16_t *sP = (f16_t *)(smem + L::P);
     float *sAD = (float *)(smem + L::AD);
-    bf16_t *sD = (bf16_t *)(smem + L::D);
+    f16_t *sD = (f16_t *)(smem + L::D);
     float *sBeta = (float *)(smem + L::BETA);
     float *sE = (float *)(smem + L::E);
-    float *sMF = (float *)(smem + L::MF);
+    float *sIE = (float *)(smem + L::IE);
     float *sEG = (float *)(smem + L::EG);
 
     // ---- work item (XCD-aware: the slices of one (item, head) share an XCD)
@@ -108,11 +157,12 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     const bool has_v = FW || !isM;
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
-    const int I = t >> 7, c = t & 127;   // prep role: 16-row block I, key channel c (value column c for V)
-    const int safe = a.gate_mode == 1;
-    const float lb = a.lb;
-    const float Ah = expf(a.a_log[h]);
-    const float dtb = a.dt_bias[h * DK + c];
+    // prep role: block I, key channels c0 .. c0+3, rows 16I + 4rq + [0, 4)
+    const int I = t >> 7, rq = t & 3, c0 = 4 * ((t >> 2) & 31);
+    const int rbase = 16 * I + 4 * rq;
+    const float negA = -expf(a.a_log[h]);
+    const float amin = a.gate_mode == 1 ? expf(a.lb) : 0.f;  // alpha floor of the safe gate
+    const f32x4 dtb = *(const f32x4 *)(a.dt_bias + h * DK + c0);
 
     // ---- state tile of wave w: rows 16ct+4g+s, column col0 + 16w + li
     f32x4 S[8];
@@ -132,144 +182,194 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     if (FW) {  // strictly-upper blocks of P are never written below
         for (int e = t; e < 64 * 64; e += NT) {
             const int i = e >> 6, j = e & 63;
-            if ((j >> 4) > (i >> 4)) sP[i * PJ + j] = (bf16_t)0.f;
+            if ((j >> 4) > (i >> 4)) sP[i * PJ + j] = (f16_t)0.f;
         }
     }
 
-    const bf16_t *kb16 = (const bf16_t *)a.k;
-    const bf16_t *qb16 = (const bf16_t *)a.q;
-    const bf16_t *vb16 = (const bf16_t *)a.v;
-
-    // ---- prefetch registers: this thread's 16 rows of raw/k/q/v and one beta logit
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    float praw[16];
-    bf16x2 pk[8], pq[8], pv[8];  // two rows per register
+    // ---- prefetch registers: 4 rows x 4 channels of raw/k/q/v, one beta logit
+    f32x4 praw[4];
+    bf16x4 pk[4], pq[4], pv[4];
     float pbl = 0.f;
-    auto issue = [&](int ck) {
+    // Loads of chunk ck in six small groups (q = 0..5).  Issued a few at a time across
+    // the previous chunk's compute, they never fill the memory request queue at once,
+    // so the waves issuing them are not held up while every workgroup's loads drain.
+    auto issue = [&](int ck, int q) {
         const int t0 = t_begin + ck * 64;
         const int n = min(64, t_end - t0);
+        auto row_of = [&](int r) { return ((int64_t)(t0 + min(rbase + r, n - 1)) * H + h); };
+        if (q == 0) {
+            praw[0] = *(const f32x4 *)(a.raw_gate + row_of(0) * DK + c0);
+            praw[1] = *(const f32x4 *)(a.raw_gate + row_of(1) * DK + c0);
+        } else if (q == 1) {
+            praw[2] = *(const f32x4 *)(a.raw_gate + row_of(2) * DK + c0);
+            praw[3] = *(const f32x4 *)(a.raw_gate + row_of(3) * DK + c0);
+            if (t < 64) pbl = a.beta_logits[(int64_t)(t0 + min(t, n - 1)) * H + h];
+        } else if (q == 2) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = t0 + min(16 * I + r, n - 1);
-            const int64_t base = ((int64_t)row * H + h) * DK + c;
-            praw[r] = a.raw_gate[base];
-            pk[r >> 1][r & 1] = kb16[base];
-            if (FW) pq[r >> 1][r & 1] = qb16[base];
-            if (has_v) pv[r >> 1][r & 1] = vb16[((int64_t)row * H + h) * DV + col0 + c];
+            for (int r = 0; r < 3; ++r) pk[r] = *(const bf16x4 *)((const bf16_t *)a.k + row_of(r) * DK + c0);
+        } else if (q == 3) {
+            pk[3] = *(const bf16x4 *)((const bf16_t *)a.k + row_of(3) * DK + c0);
+            if (FW) {
+                pq[0] = *(const bf16x4 *)((const bf16_t *)a.q + row_of(0) * DK + c0);
+                pq[1] = *(const bf16x4 *)((const bf16_t *)a.q + row_of(1) * DK + c0);
+            }
+        } else if (q == 4) {
+            if (FW) {
+                pq[2] = *(const bf16x4 *)((const bf16_t *)a.q + row_of(2) * DK + c0);
+                pq[3] = *(const bf16x4 *)((const bf16_t *)a.q + row_of(3) * DK + c0);
+            }
+            if (has_v) pv[0] = *(const bf16x4 *)((const bf16_t *)a.v + row_of(0) * DV + col0 + c0);
+        } else {
+            if (has_v)
+#pragma unroll
+                for (int r = 1; r < 4; ++r) pv[r] = *(const bf16x4 *)((const bf16_t *)a.v + row_of(r) * DV + col0 + c0);
         }
-        if (t < 64) pbl = a.beta_logits[(int64_t)(t0 + min(t, n - 1)) * H + h];
     };
-    if (n_chunks > 0) issue(0);
+    if (n_chunks > 0)
+#pragma unroll
+        for (int q = 0; q < 6; ++q) issue(0, q);
 
     for (int ck = 0; ck < n_chunks; ++ck) {
         const int t0 = t_begin + ck * 64;
         const int n = min(64, t_end - t0);
 
-        // ============ P0: gate, in-block running products, operand rows ============
-        float kc[16];
+        // ============ P0: gate, running products, score operands, V^T ============
+        bf16x4 kr4[4], qr4[4];
+        float kc[4][4];
         {
-            float al[16], kf[16], qf[16];
+            float al[4][4], kf[4][4], qf[4][4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bool valid = 16 * I + r < n;
-                al[r] = valid ? gate_alpha(praw[r], dtb, Ah, safe, lb) : 1.f;
-                kf[r] = valid ? (float)pk[r >> 1][r & 1] : 0.f;
-                qf[r] = (FW && valid) ? (float)pq[r >> 1][r & 1] : 0.f;
-            }
-            float rr = 1.f;
+            for (int r = 0; r < 4; ++r) {
+                const bool valid = rbase + r < n;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {  // Kr_i = K_i e^{G_i - G_(16I-1)}
-                rr *= al[r];
-                const int i = 16 * I + r;
-                sKR[i * PK + c] = (bf16_t)(kf[r] * rr);
-                if (FW) sQR[i * PK + c] = (bf16_t)(qf[r] * rr);
+                for (int cc = 0; cc < 4; ++cc) {
+                    const float av = gate_alpha(praw[r][cc], dtb[cc], negA, amin);
+                    al[r][cc] = valid ? av : 1.f;
+                    kf[r][cc] = valid ? (float)pk[r][cc] : 0.f;
+                    qf[r][cc] = (FW && valid) ? (float)pq[r][cc] : 0.f;
+                }
             }
-            sE[I * DK + c] = rr;
-            float cb = 1.f;
+            // products over this quarter block, then over the other quarters (quad lanes)
+            f32x4 E, pre, suf;
 #pragma unroll
-            for (int r = 15; r >= 0; --r) {  // Kc_j = K_j e^{G_(16I+15) - G_j}
-                kc[r] = kf[r] * cb;
-                sKC[(16 * I + r) * PK + c] = (bf16_t)kc[r];
-                cb *= al[r];
-            }
-            bf16x8 v0, v1;
+            for (int cc = 0; cc < 4; ++cc) {
+                float p = 1.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bf16_t x = (has_v && 16 * I + r < n) ? pv[r >> 1][r & 1] : (bf16_t)0.f;
-                if (r < 8) v0[r] = x; else v1[r - 8] = x;
+                for (int r = 0; r < 4; ++r) p *= al[r][cc];
+                const float q0 = quad_bcast<0>(p), q1 = quad_bcast<1>(p);
+                const float q2 = quad_bcast<2>(p), q3 = quad_bcast<3>(p);
+                E[cc] = ((q0 * q1) * q2) * q3;  // same operation order in every lane
+                pre[cc] = rq == 0 ? 1.f : (rq == 1 ? q0 : (rq == 2 ? q0 * q1 : (q0 * q1) * q2));
+                suf[cc] = rq == 3 ? 1.f : (rq == 2 ? q3 : (rq == 1 ? q3 * q2 : (q3 * q2) * q1));
             }
-            *(bf16x8 *)(sVT + c * PJ + 16 * I) = v0;
-            *(bf16x8 *)(sVT + c * PJ + 16 * I + 8) = v1;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                // forward: Kr_i = K_i e^{G_i - G_(16I-1)}
+                float rr = pre[cc];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    rr *= al[r][cc];
+                    kr4[r][cc] = (bf16_t)(kf[r][cc] * rr);
+                    qr4[r][cc] = (bf16_t)(qf[r][cc] * rr);
+                }
+                // backward: Kc_j = K_j e^{G_(16I+15) - G_j}
+                float cb = suf[cc];
+#pragma unroll
+                for (int r = 3; r >= 0; --r) {
+                    kc[r][cc] = kf[r][cc] * cb;
+                    cb *= al[r][cc];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = rbase + r;
+                *(bf16x4 *)(sKR + i * PK + c0) = kr4[r];
+                if (FW) *(bf16x4 *)(sQR + i * PK + c0) = qr4[r];
+                bf16x4 kcb;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) kcb[cc] = (bf16_t)kc[r][cc];
+                *(bf16x4 *)(sKC + i * PK + c0) = kcb;
+            }
+            if (rq == 0) {
+                *(f32x4 *)(sE + I * DK + c0) = E;
+                // 1/E <= e^{16 |bound|}: finite under the safe gate
+                *(f32x4 *)(sIE + I * DK + c0) = f32x4{1.f / E[0], 1.f / E[1], 1.f / E[2], 1.f / E[3]};
+            }
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                bf16x4 v4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v4[r] = (has_v && rbase + r < n) ? pv[r][cc] : (bf16_t)0.f;
+                *(bf16x4 *)(sVT + (c0 + cc) * PJ + rbase) = v4;
+            }
             if (t < 64) sBeta[t] = (t < n) ? (a.beta_mode == 0 ? 1.f / (1.f + __expf(-pbl)) : pbl) : 0.f;
         }
         __syncthreads();
 
-        // ============ P1: cross-block factors, Khat^T, pair factors ============
-        float pI = 1.f;
+        // ============ P1: cross-block factors, chain operands Kg, Qbar, Khat^T ============
         {
-            float Ev[4];
+            f32x4 Ev[4];
 #pragma unroll
-            for (int J = 0; J < 4; ++J) Ev[J] = sE[J * DK + c];
-            float qS = 1.f;
+            for (int J = 0; J < 4; ++J) Ev[J] = *(const f32x4 *)(sE + J * DK + c0);
+            f32x4 pI = f32x4{1.f, 1.f, 1.f, 1.f}, qS = pI;
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
                 if (J < I) pI *= Ev[J];
                 if (J > I) qS *= Ev[J];
             }
-            bf16x8 hh[2], hl[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float kh = kc[r] * qS;  // Khat_j = K_j e^{G_last - G_j}
-                const bf16_t hb = (bf16_t)kh;
-                hh[r >> 3][r & 7] = hb;
-                hl[r >> 3][r & 7] = (bf16_t)(kh - (float)hb);
-            }
-            *(bf16x8 *)(sKHH + c * PJ + 16 * I) = hh[0];
-            *(bf16x8 *)(sKHH + c * PJ + 16 * I + 8) = hh[1];
-            *(bf16x8 *)(sKHL + c * PJ + 16 * I) = hl[0];
-            *(bf16x8 *)(sKHL + c * PJ + 16 * I + 8) = hl[1];
-            if (I == 0) {
-                sEG[c] = Ev[0] * Ev[1] * Ev[2] * Ev[3];
-            } else if (I == 1) {
-                // factor e^{G_(16I-1) - G_(16J+15)}: 1/E_I on the diagonal, else the
-                // product of the whole blocks strictly between J and I
+            for (int r = 0; r < 4; ++r) {
+                const int i = rbase + r;
+                bf16x4 x, y;
 #pragma unroll
-                for (int p = 0; p < 10; ++p) {
-                    const int bI = kPairI[p], bJ = kPairJ[p];
-                    float f;
-                    if (bI == bJ) {
-                        f = 1.f / Ev[bI];
-                    } else {
-                        f = 1.f;
-#pragma unroll
-                        for (int K = 0; K < 4; ++K)
-                            if (K > bJ && K < bI) f *= Ev[K];
-                    }
-                    sMF[p * DK + c] = f;
+                for (int cc = 0; cc < 4; ++cc) {
+                    x[cc] = (bf16_t)((float)kr4[r][cc] * pI[cc]);  // Kg = K e^{G}
+                    y[cc] = (bf16_t)((float)qr4[r][cc] * pI[cc]);  // Qbar = Q e^{G}
                 }
+                *(bf16x4 *)(sKG + i * PK + c0) = x;
+                if (FW) *(bf16x4 *)(sQB + i * PK + c0) = y;
             }
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                f16x4 h4;  // Khat_j = K_j e^{G_last - G_j}
+#pragma unroll
+                for (int r = 0; r < 4; ++r) h4[r] = (f16_t)(kc[r][cc] * qS[cc]);
+                *(f16x4 *)(sKH + (c0 + cc) * PJ + rbase) = h4;
+            }
+            if (I == 0 && rq == 0) *(f32x4 *)(sEG + c0) = ((Ev[0] * Ev[1]) * Ev[2]) * Ev[3];
         }
         __syncthreads();
 
         // next chunk's loads fly while this chunk is computed
-        if (ck + 1 < n_chunks) issue(ck + 1);
+        const bool more = ck + 1 < n_chunks;
+        if (more) issue(ck + 1, 0);
 
         // ============ P2: decayed scores; diagonal waves also invert their block ============
         {
-            const int np = w < 4 ? 1 : (w < 6 ? 2 : 1);
-            const int p0 = w < 4 ? w : (w == 4 ? 4 : (w == 5 ? 5 : w + 2));
-            // waves 4,5 take pairs (4,6),(5,7); waves 6,7 take pairs 8,9
+            const int np = n_pairs_of_wave(w);
             for (int pp = 0; pp < np; ++pp) {
-                const int p = p0 + 2 * pp;
-                const int bI = kPairI[p], bJ = kPairJ[p];
+                int bI, bJ;
+                pair_of_wave(w, pp, bI, bJ);
                 f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
                     const int cc = 32 * kb + 8 * g;
                     const bf16x8 aK = *(const bf16x8 *)(sKR + (16 * bI + li) * PK + cc);
                     const bf16x8 kcv = *(const bf16x8 *)(sKC + (16 * bJ + li) * PK + cc);
-                    const f32x4 m0 = *(const f32x4 *)(sMF + p * DK + cc);
-                    const f32x4 m1 = *(const f32x4 *)(sMF + p * DK + cc + 4);
+                    // e^{G_(16I-1) - G_(16J+15)}: 1/E_I on the diagonal, else the product of
+                    // the decays of the whole blocks strictly between J and I (at most two)
+                    f32x4 m0, m1;
+                    if (bI == bJ) {
+                        m0 = *(const f32x4 *)(sIE + bI * DK + cc);
+                        m1 = *(const f32x4 *)(sIE + bI * DK + cc + 4);
+                    } else {
+                        m0 = f32x4{1.f, 1.f, 1.f, 1.f};
+                        m1 = m0;
+                        for (int K = bJ + 1; K < bI; ++K) {
+                            m0 *= *(const f32x4 *)(sE + K * DK + cc);
+                            m1 *= *(const f32x4 *)(sE + K * DK + cc + 4);
+                        }
+                    }
                     bf16x8 bK;
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
@@ -277,52 +377,43 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                         bK[s + 4] = (bf16_t)((float)kcv[s + 4] * m1[s]);
                     }
                     accA = mfma(aK, bK, accA);
-                    if (FW) {
-                        const bf16x8 aQ = *(const bf16x8 *)(sQR + (16 * bI + li) * PK + cc);
-                        accP = mfma(aQ, bK, accP);
-                    }
+                    if (FW) accP = mfma(*(const bf16x8 *)(sQR + (16 * bI + li) * PK + cc), bK, accP);
                 }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const int ri = 4 * g + s, i = 16 * bI + ri, j = 16 * bJ + li;
                     const float av = sBeta[i] * accA[s];
                     if (bI == bJ)
-                        sAD[(bI * 16 + ri) * 17 + li] = (li < ri) ? av : 0.f;
+                        sAD[(bI * 16 + ri) * 20 + li] = (li < ri) ? av : 0.f;
                     else
-                        sAO[i * PJ + j] = (bf16_t)(-av);
-                    if (FW) sP[i * PJ + j] = (bf16_t)((j <= i) ? accP[s] : 0.f);
+                        sAO[i * PJ + j] = (f16_t)(-av);
+                    if (FW) sP[i * PJ + j] = (f16_t)((j <= i) ? accP[s] : 0.f);
                 }
             }
+            if (more) issue(ck + 1, 1);
             if (w < 4 && l < 16) {
-                // (I + A_ww)^-1 by forward substitution, one column per lane
+                // (I + A_ww)^-1, one column per lane, right-looking substitution: as soon as
+                // x_k is final it is folded into every later row, so the dependent chain is
+                // one FMA per row instead of a full dot product per row.
                 const int col = l;
-                const float *Ab = sAD + w * 16 * 17;
-                float x[16];
+                const float *Ab = sAD + w * 16 * 20;
+                float x[16], acc[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.f : 0.f;
+                for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-                for (int r = 1; r < 16; ++r) {
-                    float s = 0.f;
+                for (int k = 0; k < 16; ++k) {
+                    x[k] = (k == col) ? 1.f : ((k < col) ? 0.f : -acc[k]);
 #pragma unroll
-                    for (int kk = 0; kk < r; ++kk) s += (kk >= col) ? Ab[r * 17 + kk] * x[kk] : 0.f;
-                    if (r > col) x[r] = -s;
+                    for (int r = k + 1; r < 16; ++r) acc[r] = fmaf(Ab[r * 20 + k], x[k], acc[r]);
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sD[(w * 16 + r) * 24 + col] = (bf16_t)x[r];
+                for (int r = 0; r < 16; ++r) sD[(w * 16 + r) * 24 + col] = (f16_t)x[r];
             }
         }
         __syncthreads();
 
-        // ============ P3: Kg = Kr e^{G_(16I-1)} and Qbar = Qr e^{G_(16I-1)} in place ============
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = 16 * I + r;
-            sKR[i * PK + c] = (bf16_t)((float)sKR[i * PK + c] * pI);
-            if (FW) sQR[i * PK + c] = (bf16_t)((float)sQR[i * PK + c] * pI);
-        }
-        __syncthreads();
-
-        // ============ P4: chain step of value tile w ============
+        // ============ P3: chain step of value tile w ============
+        if (more) issue(ck + 1, 2);
         {
             bf16x8 Sb[4];
 #pragma unroll
@@ -334,13 +425,15 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 Z[rt] = zero4();
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    Y[rt] = mfma(fragA_perm(sKR, PK, 16 * rt + li, 32 * kb, g), Sb[kb], Y[rt]);
-                    if (FW) Z[rt] = mfma(fragA_perm(sQR, PK, 16 * rt + li, 32 * kb, g), Sb[kb], Z[rt]);
+                    Y[rt] = mfma(fragA_perm(sKG, PK, 16 * rt + li, 32 * kb, g), Sb[kb], Y[rt]);
+                    // output transposed, O^T = S^T Qbar^T: the state tile is the A operand
+                    if (FW) Z[rt] = mfma(Sb[kb], fragA_perm(sQB, PK, 16 * rt + li, 32 * kb, g), Z[rt]);
                 }
             }
+            if (more) issue(ck + 1, 3);
             // R = beta (V - Kg S); solve (I + A) U = R block by block
             const int vcol = 16 * w + li;
-            bf16x4 Uh[4], Ul[4];
+            f16x4 Uh[4], Ul[4];
 #pragma unroll
             for (int bI = 0; bI < 4; ++bI) {
                 const f32x4 vv = f4(*(const bf16x4 *)(sVT + vcol * PJ + 16 * bI + 4 * g));
@@ -348,45 +441,44 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 f32x4 acc = bb * (vv - Y[bI]);
 #pragma unroll
                 for (int bJ = 0; bJ < bI; ++bJ) {
-                    const bf16x4 ao = *(const bf16x4 *)(sAO + (16 * bI + li) * PJ + 16 * bJ + 4 * g);
-                    acc = mfma16(ao, Uh[bJ], acc);
-                    acc = mfma16(ao, Ul[bJ], acc);
+                    const f16x4 ao = *(const f16x4 *)(sAO + (16 * bI + li) * PJ + 16 * bJ + 4 * g);
+                    acc = mfma16h(ao, Uh[bJ], acc);
+                    acc = mfma16h(ao, Ul[bJ], acc);
                 }
-                bf16x4 wh, wl;
-                split4(acc, wh, wl);
-                const bf16x4 dd = *(const bf16x4 *)(sD + (bI * 16 + li) * 24 + 4 * g);
-                f32x4 u = mfma16(dd, wh, zero4());
-                u = mfma16(dd, wl, u);
-                split4(u, Uh[bI], Ul[bI]);
+                f16x4 wh, wl;
+                split_h(acc, wh, wl);
+                const f16x4 dd = *(const f16x4 *)(sD + (bI * 16 + li) * 24 + 4 * g);
+                f32x4 u = mfma16h(dd, wh, zero4());
+                u = mfma16h(dd, wl, u);
+                split_h(u, Uh[bI], Ul[bI]);
             }
+            if (more) issue(ck + 1, 4);
             if (FW) {
                 bf16_t *outp = (bf16_t *)a.out;
-                const int col = col0 + vcol;
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
+                    // O^T += U^T P^T
 #pragma unroll
                     for (int jb = 0; jb <= (rt >> 1); ++jb)
-                        Z[rt] = mfma(fragA_perm(sP, PJ, 16 * rt + li, 32 * jb, g), cat(Uh[2 * jb], Uh[2 * jb + 1]),
-                                     Z[rt]);
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const int i = 16 * rt + 4 * g + s;
-                        if (i < n) outp[((int64_t)(t0 + i) * H + h) * DV + col] = (bf16_t)(a.scale * Z[rt][s]);
-                    }
+                        Z[rt] = mfma32h(cath(Uh[2 * jb], Uh[2 * jb + 1]),
+                                        fragA_perm_h(sP, PJ, 16 * rt + li, 32 * jb, g), Z[rt]);
+                    // lane holds O[token 16rt + li][columns 16w + 4g .. +3]: one 8-byte store
+                    const int i = 16 * rt + li;
+                    if (i < n)
+                        *(bf16x4 *)(outp + ((int64_t)(t0 + i) * H + h) * DV + col0 + 16 * w + 4 * g) =
+                            bf4(a.scale * Z[rt]);
                 }
             }
+            if (more) issue(ck + 1, 5);
+            // S <- Diag(e^{G_last}) S + Khat^T U
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) {
                 S[ct] *= *(const f32x4 *)(sEG + 16 * ct + 4 * g);
 #pragma unroll
                 for (int jb = 0; jb < 2; ++jb) {
-                    const bf16x8 ah = fragA_perm(sKHH, PJ, 16 * ct + li, 32 * jb, g);
-                    const bf16x8 alo = fragA_perm(sKHL, PJ, 16 * ct + li, 32 * jb, g);
-                    const bf16x8 bh = cat(Uh[2 * jb], Uh[2 * jb + 1]);
-                    const bf16x8 bl = cat(Ul[2 * jb], Ul[2 * jb + 1]);
-                    S[ct] = mfma(ah, bh, S[ct]);
-                    S[ct] = mfma(ah, bl, S[ct]);
-                    S[ct] = mfma(alo, bh, S[ct]);
+                    const f16x8 kh = fragA_perm_h(sKH, PJ, 16 * ct + li, 32 * jb, g);
+                    S[ct] = mfma32h(kh, cath(Uh[2 * jb], Uh[2 * jb + 1]), S[ct]);
+                    S[ct] = mfma32h(kh, cath(Ul[2 * jb], Ul[2 * jb + 1]), S[ct]);
                 }
             }
         }
