@@ -19,6 +19,9 @@
 //    once per chunk) and the right-hand side split into fp16 hi + lo;
 //  * the state update uses fp16 Khat (|Khat| <= 1) against fp16 hi + lo U; products
 //    with the state itself (Kg S, Qbar S) are bf16, whose range matches fp32;
+//  * the key channels of the state are stored in a permuted row order inside its MFMA
+//    tiles (key_row below), so that a lane's eight k slots of Kg S and Qbar S are eight
+//    consecutive channels and each operand fragment is one 16-byte LDS read;
 //  * global loads of chunk c+1 are issued before the scores of chunk c are built and
 //    land in plain 32-bit registers, so nothing waits on them until chunk c+1.
 #include "kda_common.h"
@@ -68,6 +71,18 @@ __device__ __forceinline__ f32x4 mfma32h(f16x8 a, f16x8 b, f32x4 c) {
 }
 __device__ __forceinline__ f16x8 cath(f16x4 a, f16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Key channel held in row rho of the state's 16-row tile ct.  Tiles 2kb and 2kb+1 hold
+// channels 32kb + 8(rho/4) + {0..3} and {4..7}: the k slots s of lane group g in the
+// products with the state are then channels 32kb + 8g + s.
+__device__ __forceinline__ int key_row(int ct, int rho) {
+    return 32 * (ct >> 1) + 8 * (rho >> 2) + 4 * (ct & 1) + (rho & 3);
+}
+// Inverse: the tile row (16 ct + rho) of key channel c.  Khat^T is stored in this row
+// order so that the state update reads 16 consecutive rows per fragment.
+__device__ __forceinline__ int tile_row(int c) {
+    return 16 * (2 * (c >> 5) + ((c >> 2) & 1)) + 4 * ((c >> 3) & 3) + (c & 3);
 }
 
 // A-operand fragment whose k slots follow the accumulator row order of two 16-row
@@ -174,7 +189,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int r = 16 * ct + 4 * g + s;
+                const int r = key_row(ct, 4 * g + s);
                 S[ct][s] = FW ? a.state_pool[(((int64_t)slot * H + h) * DK + r) * DV + col]
                               : ((isM && r == col) ? 1.f : 0.f);
             }
@@ -237,6 +252,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
         bf16x4 kr4[4], qr4[4];
         float kc[4][4];
         {
+            // Rows past the sequence end hold a copy of its last row: only their gate
+            // (alpha = 1) and beta (0) are masked; with beta = 0 they add nothing to A, R, U
+            // or the state, and their outputs are never stored.
             float al[4][4], kf[4][4], qf[4][4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -245,8 +263,8 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 for (int cc = 0; cc < 4; ++cc) {
                     const float av = gate_alpha(praw[r][cc], dtb[cc], negA, amin);
                     al[r][cc] = valid ? av : 1.f;
-                    kf[r][cc] = valid ? (float)pk[r][cc] : 0.f;
-                    qf[r][cc] = (FW && valid) ? (float)pq[r][cc] : 0.f;
+                    kf[r][cc] = (float)pk[r][cc];
+                    qf[r][cc] = FW ? (float)pq[r][cc] : 0.f;
                 }
             }
             // products over this quarter block, then over the other quarters (quad lanes)
@@ -259,8 +277,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 const float q0 = quad_bcast<0>(p), q1 = quad_bcast<1>(p);
                 const float q2 = quad_bcast<2>(p), q3 = quad_bcast<3>(p);
                 E[cc] = ((q0 * q1) * q2) * q3;  // same operation order in every lane
-                pre[cc] = rq == 0 ? 1.f : (rq == 1 ? q0 : (rq == 2 ? q0 * q1 : (q0 * q1) * q2));
-                suf[cc] = rq == 3 ? 1.f : (rq == 2 ? q3 : (rq == 1 ? q3 * q2 : (q3 * q2) * q1));
+                // decay of the quarters before / after this lane's quarter (selects, no branches)
+                pre[cc] = (rq >= 1 ? q0 : 1.f) * (rq >= 2 ? q1 : 1.f) * (rq >= 3 ? q2 : 1.f);
+                suf[cc] = (rq <= 2 ? q3 : 1.f) * (rq <= 1 ? q2 : 1.f) * (rq <= 0 ? q1 : 1.f);
             }
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
@@ -299,7 +318,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             for (int cc = 0; cc < 4; ++cc) {
                 bf16x4 v4;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v4[r] = (has_v && rbase + r < n) ? pv[r][cc] : (bf16_t)0.f;
+                for (int r = 0; r < 4; ++r) v4[r] = has_v ? pv[r][cc] : (bf16_t)0.f;
                 *(bf16x4 *)(sVT + (c0 + cc) * PJ + rbase) = v4;
             }
             if (t < 64) sBeta[t] = (t < n) ? (a.beta_mode == 0 ? 1.f / (1.f + __expf(-pbl)) : pbl) : 0.f;
@@ -334,7 +353,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 f16x4 h4;  // Khat_j = K_j e^{G_last - G_j}
 #pragma unroll
                 for (int r = 0; r < 4; ++r) h4[r] = (f16_t)(kc[r][cc] * qS[cc]);
-                *(f16x4 *)(sKH + (c0 + cc) * PJ + rbase) = h4;
+                *(f16x4 *)(sKH + tile_row(c0 + cc) * PJ + rbase) = h4;
             }
             if (I == 0 && rq == 0) *(f32x4 *)(sEG + c0) = ((Ev[0] * Ev[1]) * Ev[2]) * Ev[3];
         }
@@ -425,9 +444,10 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 Z[rt] = zero4();
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    Y[rt] = mfma(fragA_perm(sKG, PK, 16 * rt + li, 32 * kb, g), Sb[kb], Y[rt]);
+                    Y[rt] = mfma(*(const bf16x8 *)(sKG + (16 * rt + li) * PK + 32 * kb + 8 * g), Sb[kb], Y[rt]);
                     // output transposed, O^T = S^T Qbar^T: the state tile is the A operand
-                    if (FW) Z[rt] = mfma(Sb[kb], fragA_perm(sQB, PK, 16 * rt + li, 32 * kb, g), Z[rt]);
+                    if (FW)
+                        Z[rt] = mfma(Sb[kb], *(const bf16x8 *)(sQB + (16 * rt + li) * PK + 32 * kb + 8 * g), Z[rt]);
                 }
             }
             if (more) issue(ck + 1, 3);
@@ -473,7 +493,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             // S <- Diag(e^{G_last}) S + Khat^T U
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) {
-                S[ct] *= *(const f32x4 *)(sEG + 16 * ct + 4 * g);
+                S[ct] *= *(const f32x4 *)(sEG + key_row(ct, 4 * g));
 #pragma unroll
                 for (int jb = 0; jb < 2; ++jb) {
                     const f16x8 kh = fragA_perm_h(sKH, PJ, 16 * ct + li, 32 * jb, g);
@@ -492,7 +512,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int r = 16 * ct + 4 * g + s;
+                const int r = key_row(ct, 4 * g + s);
                 if (FW)
                     a.state_pool[(((int64_t)slot * H + h) * DK + r) * DV + col] = S[ct][s];
                 else if (isM)
