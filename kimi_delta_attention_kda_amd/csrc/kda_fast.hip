@@ -107,8 +107,9 @@ __device__ __forceinline__ void split_h(f32x4 x, f16x4 &hi, f16x4 &lo) {
 // alpha = exp(-A softplus(x)) = (1 + e^x)^(-A), computed as 2^(-A log2(1 + 2^(x log2 e)));
 // the safe gate's floor on log alpha is a floor exp(bound) on alpha.  Branch-free: the
 // three transcendentals are the hardware base-2 exp/log.
-__device__ __forceinline__ float gate_alpha(float raw, float dtb, float negA, float amin) {
-    const float t = __builtin_amdgcn_exp2f((raw + dtb) * 1.44269504088896341f);
+__device__ __forceinline__ float gate_alpha(float raw, float dtb_l2e, float negA, float amin) {
+    // dtb_l2e = dt_bias * log2(e): one FMA forms (raw + dt_bias) log2(e)
+    const float t = __builtin_amdgcn_exp2f(fmaf(raw, 1.44269504088896341f, dtb_l2e));
     const float a = __builtin_amdgcn_exp2f(negA * __builtin_amdgcn_logf(1.f + t));
     return fmaxf(a, amin);
 }
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     const int rbase = 16 * I + 4 * rq;
     const float negA = -expf(a.a_log[h]);
     const float amin = a.gate_mode == 1 ? expf(a.lb) : 0.f;  // alpha floor of the safe gate
-    const f32x4 dtb = *(const f32x4 *)(a.dt_bias + h * DK + c0);
+    const f32x4 dtb = *(const f32x4 *)(a.dt_bias + h * DK + c0) * 1.44269504088896341f;
 
     // ---- state tile of wave w: rows 16ct+4g+s, column col0 + 16w + li
     f32x4 S[8];
@@ -257,15 +258,19 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             // or the state, and their outputs are never stored.
             float al[4][4], kf[4][4], qf[4][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool valid = rbase + r < n;
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
-                    const float av = gate_alpha(praw[r][cc], dtb[cc], negA, amin);
-                    al[r][cc] = valid ? av : 1.f;
+                    al[r][cc] = gate_alpha(praw[r][cc], dtb[cc], negA, amin);
                     kf[r][cc] = (float)pk[r][cc];
                     qf[r][cc] = FW ? (float)pq[r][cc] : 0.f;
                 }
+            if (n < 64) {  // last, partial chunk of the sequence (wave-uniform branch)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc)
+                        if (rbase + r >= n) al[r][cc] = 1.f;
             }
             // products over this quarter block, then over the other quarters (quad lanes)
             f32x4 E, pre, suf;
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             }
             if (I == 0 && rq == 0) *(f32x4 *)(sEG + c0) = ((Ev[0] * Ev[1]) * Ev[2]) * Ev[3];
         }
-        __syncthreads();
+        // (no barrier: Kg, Qbar, Khat^T and e^{G_last} are first read in the chain step)
 
         // next chunk's loads fly while this chunk is computed
         const bool more = ck + 1 < n_chunks;
