@@ -174,7 +174,7 @@ def main():
                    "gate": gate, "gate_lower_bound": w.lower_bound, "pool_slots": w.n_slots},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "kda_chain_kernel", "kernel_ms": round(kern_ms, 4),
+                     "kernel": "kda_fast_kernel", "kernel_ms": round(kern_ms, 4),
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"algorithmic_tflops": round(fl / (kern_ms / 1e3) / 1e12, 2),
                  "frac_of_bf16_peak": round(fl / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
