@@ -4,8 +4,10 @@
  * Every tensor argument is a DEVICE pointer to row-major, contiguous memory
  * owned by the caller.  Calls validate their host-visible arguments, enqueue
  * their kernels on `stream` (a hipStream_t; NULL = the default stream) and
- * return without synchronising.  Nothing is allocated on the device: the
- * kernels keep every intermediate in registers and LDS.
+ * return without synchronising.  The chunk kernels keep every intermediate of
+ * a chunk in registers and LDS; only the load-balanced forward pass needs a
+ * device workspace (kda_chunk_fwd_ws), which kda_chunk_fwd draws from a
+ * stream-ordered memory pool owned by the library.
  *
  * Per head the method keeps a state S [dk, dv] (key axis = rows) and for each
  * token t applies
@@ -20,8 +22,8 @@
  * or the logits taken as probabilities (max.nn.state_space.kda_chunk,
  * Parameters: raw_gate, beta_logits, a_log, dt_bias, gate_mode, beta_mode).
  * The prefill is evaluated over 64-token chunks with the same result as the
- * token recurrence (kda_chunk: "same recurrence ... evaluated in parallel
- * across ... chunks"; its AMD gfx950 pipeline uses 64-token chunks).
+ * token recurrence (kda_chunk describes the recurrence computed chunk-parallel;
+ * its AMD gfx950 pipeline uses 64-token chunks).
  *
  * Errors: a status other than KDA_OK is returned BEFORE anything is launched
  * when a host-checkable argument is wrong (null pointer, extent, dtype, mode,
@@ -33,6 +35,7 @@
 #ifndef LIBKDA_H
 #define LIBKDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -106,6 +109,38 @@ kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, con
                          const int32_t *state_indices, void *out, void *stream);
 
 /*
+ * kda_chunk_fwd with a caller-owned workspace.  For bf16 with dk = dv = 128
+ * the forward pass is load-balanced over the GPU's compute units: a sequence
+ * much longer than the average load per CU is cut into pieces at chunk
+ * boundaries that run in parallel, using the segment maps of KDA Context
+ * Parallelism (Theory: a piece started from state X ends in M X + U, and its
+ * outputs are q^T M_t X + q^T U_t); the pieces' states are then composed in
+ * order and the outputs corrected.  Results equal those of the unsplit pass
+ * up to rounding (the correction term is formed with bf16 MFMA operands).
+ *   workspace       device memory of at least kda_chunk_fwd_workspace_size()
+ *                   bytes, 256-byte aligned, not shared with a call that may
+ *                   run concurrently; its contents need no initialisation.
+ *                   NULL (or workspace_bytes == 0): no load balancing, one
+ *                   workgroup per (sequence, head), no workspace.
+ * Other arguments as for kda_chunk_fwd.  KDA_ERR_SHAPE if workspace is given
+ * but smaller than required.  For other dtypes and dims the workspace is not
+ * used.
+ */
+kda_status kda_chunk_fwd_ws(const kda_desc *desc, const void *q, const void *k, const void *v,
+                            const float *raw_gate, const float *beta_logits, const float *a_log,
+                            const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
+                            const int32_t *state_indices, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes kda_chunk_fwd_ws needs for desc on the current device
+ * (0 when the load-balanced path does not apply).  It grows with
+ * total_tokens * num_heads * dv (bf16 correction rows) plus a few MiB per
+ * compute unit for piece states.
+ */
+kda_status kda_chunk_fwd_workspace_size(const kda_desc *desc, size_t *bytes);
+
+/*
  * Affine summaries of token segments (KDA Context Parallelism, "Theory": each
  * segment is the map F_i(S) = M_i S + U_i of its incoming state).  Segment i
  * covers tokens [seg_offsets[i], seg_offsets[i+1]) of one sequence; for each
@@ -132,7 +167,7 @@ kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *
  * order with the state multiplied on the left.
  *   M [n_seg, H, dk, dk], U [n_seg, H, dk, dv], S_init [H, dk, dv] (read only);
  *   incoming, outgoing [n_seg, H, dk, dv], final_state [H, dk, dv] (written).
- * f32 throughout; dk in {16, 32, ..., 256} (multiple of 16), dv a multiple of 16.
+ * f32 throughout; dk in {16, 32, 64, 128}, dv a multiple of 16.
  * n_seg >= 1 (at least one segment; KDA_ERR_SHAPE otherwise).
  */
 kda_status kda_affine_exclusive_scan(int32_t n_seg, int32_t num_heads, int32_t dk, int32_t dv,

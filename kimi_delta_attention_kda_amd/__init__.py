@@ -51,13 +51,15 @@ def lib():
         vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
         dp = C.POINTER(KdaDesc)
         L.kda_chunk_fwd.argtypes = [dp] + [vp] * 12
+        L.kda_chunk_fwd_ws.argtypes = [dp] + [vp] * 12 + [C.c_size_t, vp]
+        L.kda_chunk_fwd_workspace_size.argtypes = [dp, C.POINTER(C.c_size_t)]
         L.kda_segment_summary.argtypes = [dp] + [vp] * 7 + [i32, vp, vp, vp]
         L.kda_affine_exclusive_scan.argtypes = [i32, i32, i32, i32] + [vp] * 7
         L.kda_validate_varlen.argtypes = [vp, i32, i64, vp, i32]
         L.kda_status_string.argtypes = [C.c_int]
         L.kda_status_string.restype = C.c_char_p
-        for f in ("kda_chunk_fwd", "kda_segment_summary", "kda_affine_exclusive_scan",
-                  "kda_validate_varlen"):
+        for f in ("kda_chunk_fwd", "kda_chunk_fwd_ws", "kda_chunk_fwd_workspace_size",
+                  "kda_segment_summary", "kda_affine_exclusive_scan", "kda_validate_varlen"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -103,14 +105,20 @@ def make_desc(T, B, H, dk, dv, max_slots, qkv_dtype, out_dtype, gate_mode="safe"
 
 def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool, state_indices,
               *, output_dtype=None, gate_mode="safe", lower_bound=-5.0, beta_mode="logits",
-              state_layout="K_FIRST", scale=None, out=None):
+              state_layout="K_FIRST", scale=None, out=None, workspace="torch"):
     """Chunk-parallel varlen KDA prefill; mutates state_pool[state_indices] in place.
 
     Shapes follow max.nn.state_space.kda_chunk: q,k [T,H,dk]; v [T,H,dv]; raw_gate
     [T,H,dk] f32; beta_logits [T,H] f32; a_log [H] f32; dt_bias [H,dk] f32; cu_seqlens
     [B+1] int32; state_pool [slots,H,dk,dv] f32; state_indices [B] int32.  Returns out
     [T,H,dv] in output_dtype (default: q's dtype).
+
+    workspace: "torch" (load-balanced pass, workspace from torch's allocator on the
+    current stream), "library" (kda_chunk_fwd: the library's own stream-ordered pool) or
+    "none" (no load balancing).
     """
+    if workspace not in ("torch", "library", "none"):
+        raise ValueError("workspace must be 'torch', 'library' or 'none'")
     T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -134,9 +142,19 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
         _need(out, "out", odt, dev)
     d = make_desc(T, B, H, dk, dv, state_pool.shape[0], q.dtype, odt, gate_mode, lower_bound,
                   beta_mode, state_layout, scale)
-    _check(lib().kda_chunk_fwd(C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate),
-                               _ptr(beta_logits), _ptr(a_log), _ptr(dt_bias), _ptr(cu_seqlens),
-                               _ptr(state_pool), _ptr(state_indices), _ptr(out), _stream()))
+    args = (C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(beta_logits), _ptr(a_log),
+            _ptr(dt_bias), _ptr(cu_seqlens), _ptr(state_pool), _ptr(state_indices), _ptr(out))
+    if workspace == "library":
+        _check(lib().kda_chunk_fwd(*args, _stream()))
+        return out
+    ws, nbytes = None, 0
+    if workspace == "torch":
+        need = C.c_size_t(0)
+        _check(lib().kda_chunk_fwd_workspace_size(C.byref(d), C.byref(need)))
+        if need.value > 0:
+            ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+            nbytes = need.value
+    _check(lib().kda_chunk_fwd_ws(*args, _ptr(ws), nbytes, _stream()))
     return out
 
 

@@ -1,6 +1,8 @@
 // kda_api.hip -- C ABI of libkda: argument validation, launch planning, status codes.
+#include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/libkda.h"
@@ -60,6 +62,126 @@ int value_slice(int dk, bool precise) {
 
 bool use_fast(const kda_desc *d) { return d->qkv_dtype == KDA_BF16 && d->dk == 128 && d->dv == 128; }
 
+constexpr int MAX_DEV = 64;
+
+// Compute units of the current device (cached per device); -1 on failure.
+int current_device_cus(int *dev_out) {
+    static std::mutex mu;
+    static int cus[MAX_DEV] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return -1;
+    *dev_out = dev;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return -1;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Library-owned stream-ordered pool of device dev, created on first use; it keeps
+// freed blocks for reuse (release threshold = unlimited).  nullptr if unavailable.
+hipMemPool_t device_pool(int dev) {
+    static std::mutex mu;
+    static hipMemPool_t pools[MAX_DEV] = {};
+    static bool failed[MAX_DEV] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[dev] && !failed[dev]) {
+        hipMemPoolProps props;
+        memset(&props, 0, sizeof(props));
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
+            uint64_t thr = UINT64_MAX;
+            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+            pools[dev] = pool;
+        } else {
+            failed[dev] = true;
+            (void)hipGetLastError();
+        }
+    }
+    return pools[dev];
+}
+
+bool planned_applies(const kda_desc *d) { return use_fast(d) && d->batch > 0 && d->total_tokens > 0; }
+
+kda_status workspace_bytes_for(const kda_desc *d, size_t *bytes, kda::PlanLayout *lay, int *n_cu) {
+    *bytes = 0;
+    if (!planned_applies(d)) return KDA_OK;
+    int dev = 0;
+    const int cus = current_device_cus(&dev);
+    if (cus <= 0) return KDA_ERR_HIP;
+    *lay = kda::plan_layout(d->total_tokens, d->batch, d->num_heads, d->dk, d->dv, cus);
+    *bytes = lay->total;
+    *n_cu = cus;
+    return KDA_OK;
+}
+
+// Every host-checkable argument of the forward pass.
+kda_status check_fwd(const kda_desc *desc, const void *q, const void *k, const void *v,
+                     const float *raw_gate, const float *beta_logits, const float *a_log,
+                     const float *dt_bias, const int32_t *cu_seqlens, const float *state_pool,
+                     const int32_t *state_indices, const void *out) {
+    kda_status st = check_desc(desc, false);
+    if (st != KDA_OK) return st;
+    if (!a_log || !dt_bias || !cu_seqlens || !state_pool || (desc->batch > 0 && !state_indices))
+        return KDA_ERR_NULL;
+    if (desc->total_tokens > 0 && (!q || !k || !v || !raw_gate || !beta_logits || !out)) return KDA_ERR_NULL;
+    return KDA_OK;
+}
+
+kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, const void *v,
+                          const float *raw_gate, const float *beta_logits, const float *a_log,
+                          const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
+                          const int32_t *state_indices, void *out, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    kda_status st = check_fwd(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
+                              state_indices, out);
+    if (st != KDA_OK) return st;
+    if (desc->batch == 0 || desc->total_tokens == 0) {
+        // no tokens: nothing to read or write (every sequence is empty)
+        return KDA_OK;
+    }
+    const bool precise = desc->qkv_dtype == KDA_F32;
+    kda::ChainArgs a = base_args(desc);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.raw_gate = raw_gate;
+    a.beta_logits = beta_logits;
+    a.a_log = a_log;
+    a.dt_bias = dt_bias;
+    a.offsets = cu_seqlens;
+    a.state_pool = state_pool;
+    a.state_indices = state_indices;
+    a.out = out;
+    a.n_items = desc->batch;
+    hipError_t e;
+    if (use_fast(desc)) {
+        a.n_slices = 1;
+        if (workspace && workspace_bytes > 0) {
+            size_t need = 0;
+            kda::PlanLayout lay;
+            int n_cu = 0;
+            st = workspace_bytes_for(desc, &need, &lay, &n_cu);
+            if (st != KDA_OK) return st;
+            if (workspace_bytes < need) return KDA_ERR_SHAPE;
+            e = kda::launch_planned_fwd(a, (char *)workspace, lay, n_cu, (hipStream_t)stream);
+        } else {
+            e = kda::launch_fast(a, kda::MODE_FWD, (hipStream_t)stream);
+        }
+    } else {
+        const int dvs = value_slice(desc->dk, precise);
+        a.n_slices = desc->dv / dvs;
+        e = kda::launch_chain(a, desc->dk, dvs, precise, kda::MODE_FWD, (hipStream_t)stream);
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,39 +206,48 @@ kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, con
                          const float *raw_gate, const float *beta_logits, const float *a_log,
                          const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
                          const int32_t *state_indices, void *out, void *stream) {
+    kda_status st = check_fwd(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
+                              state_indices, out);
+    if (st != KDA_OK) return st;  // nothing allocated or launched
+    if (planned_applies(desc)) {
+        size_t need = 0;
+        kda::PlanLayout lay;
+        int n_cu = 0;
+        int dev = 0;
+        if (workspace_bytes_for(desc, &need, &lay, &n_cu) == KDA_OK && need > 0 &&
+            current_device_cus(&dev) > 0) {
+            hipMemPool_t pool = device_pool(dev);
+            void *ws = nullptr;
+            if (pool && hipMallocFromPoolAsync(&ws, need, pool, (hipStream_t)stream) == hipSuccess) {
+                st = chunk_fwd_impl(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens,
+                                    state_pool, state_indices, out, ws, need, stream);
+                (void)hipFreeAsync(ws, (hipStream_t)stream);
+                return st;
+            }
+            (void)hipGetLastError();  // no workspace: fall back to the unbalanced launch
+        }
+    }
+    return chunk_fwd_impl(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
+                          state_indices, out, nullptr, 0, stream);
+}
+
+kda_status kda_chunk_fwd_ws(const kda_desc *desc, const void *q, const void *k, const void *v,
+                            const float *raw_gate, const float *beta_logits, const float *a_log,
+                            const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
+                            const int32_t *state_indices, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    return chunk_fwd_impl(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
+                          state_indices, out, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_workspace_size(const kda_desc *desc, size_t *bytes) {
+    if (!bytes) return KDA_ERR_NULL;
+    *bytes = 0;
     kda_status st = check_desc(desc, false);
     if (st != KDA_OK) return st;
-    if (!a_log || !dt_bias || !cu_seqlens || !state_pool || (desc->batch > 0 && !state_indices))
-        return KDA_ERR_NULL;
-    if (desc->total_tokens > 0 && (!q || !k || !v || !raw_gate || !beta_logits || !out)) return KDA_ERR_NULL;
-    if (desc->batch == 0 || desc->total_tokens == 0) {
-        // no tokens: nothing to read or write (every sequence is empty)
-        return KDA_OK;
-    }
-    const bool precise = desc->qkv_dtype == KDA_F32;
-    kda::ChainArgs a = base_args(desc);
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.raw_gate = raw_gate;
-    a.beta_logits = beta_logits;
-    a.a_log = a_log;
-    a.dt_bias = dt_bias;
-    a.offsets = cu_seqlens;
-    a.state_pool = state_pool;
-    a.state_indices = state_indices;
-    a.out = out;
-    a.n_items = desc->batch;
-    hipError_t e;
-    if (use_fast(desc)) {
-        a.n_slices = 1;
-        e = kda::launch_fast(a, kda::MODE_FWD, (hipStream_t)stream);
-    } else {
-        const int dvs = value_slice(desc->dk, precise);
-        a.n_slices = desc->dv / dvs;
-        e = kda::launch_chain(a, desc->dk, dvs, precise, kda::MODE_FWD, (hipStream_t)stream);
-    }
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    kda::PlanLayout lay;
+    int n_cu = 0;
+    return workspace_bytes_for(desc, bytes, &lay, &n_cu);
 }
 
 kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *v,

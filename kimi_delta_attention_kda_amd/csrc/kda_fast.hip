@@ -154,58 +154,108 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     float *sIE = (float *)(smem + L::IE);
     float *sEG = (float *)(smem + L::EG);
 
-    // ---- work item (XCD-aware: the slices of one (item, head) share an XCD)
     const int H = a.H;
-    const int n_units = a.n_items * H;
-    const int lin = blockIdx.x;
-    const int xcd = lin & 7, jx = lin >> 3;
-    const int slice = jx % a.n_slices;
-    const int unit = (jx / a.n_slices) * 8 + xcd;
-    if (unit >= n_units) return;
-    const int item = unit / H, h = unit - item * H;
-    const int t_begin = a.offsets[item], t_end = a.offsets[item + 1];
-    const int len = t_end - t_begin;
-    if (FW && len <= 0) return;
-    const int n_chunks = len > 0 ? (len + 63) / 64 : 0;
-    const int aug0 = slice * 128;
-    const bool isM = (!FW) && aug0 < DK;
-    const int col0 = (FW || isM) ? aug0 : aug0 - DK;
-    const bool has_v = FW || !isM;
-
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
     // prep role: block I, key channels c0 .. c0+3, rows 16I + 4rq + [0, 4)
     const int I = t >> 7, rq = t & 3, c0 = 4 * ((t >> 2) & 31);
     const int rbase = 16 * I + 4 * rq;
-    const float negA = -expf(a.a_log[h]);
     const float amin = a.gate_mode == 1 ? expf(a.lb) : 0.f;  // alpha floor of the safe gate
-    const f32x4 dtb = *(const f32x4 *)(a.dt_bias + h * DK + c0) * 1.44269504088896341f;
+    const int xcd = blockIdx.x & 7;  // workgroups are dealt to the 8 XCDs round-robin
 
-    // ---- state tile of wave w: rows 16ct+4g+s, column col0 + 16w + li
-    f32x4 S[8];
-    int slot = 0;
-    if (FW) slot = a.state_indices[item];
-    {
-        const int col = col0 + 16 * w + li;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int r = key_row(ct, 4 * g + s);
-                S[ct][s] = FW ? a.state_pool[(((int64_t)slot * H + h) * DK + r) * DV + col]
-                              : ((isM && r == col) ? 1.f : 0.f);
-            }
-    }
     if (FW) {  // strictly-upper blocks of P are never written below
         for (int e = t; e < 64 * 64; e += NT) {
             const int i = e >> 6, j = e & 63;
             if ((j >> 4) > (i >> 4)) sP[i * PJ + j] = (f16_t)0.f;
         }
     }
+    __shared__ int s_next;
+
+    // One unit per pass: one (item, head) of the grid, or one queued unit of a plan.
+    for (int pass = 0;; ++pass) {
+        int t_begin, t_end, h;
+        int init;      // 0: load the state from fin, 1: identity, 2: zero
+        bool has_v;
+        float *fin;    // [DK][DV] state of this unit: initial (init 0) and final
+        bf16_t *obase = (bf16_t *)a.out;
+        if (!a.plan) {
+            if (pass > 0) break;
+            const int jx = blockIdx.x >> 3;
+            const int slice = jx % a.n_slices;
+            const int unit = (jx / a.n_slices) * 8 + xcd;
+            if (unit >= a.n_items * H) break;
+            const int item = unit / H;
+            h = unit - item * H;
+            t_begin = a.offsets[item];
+            t_end = a.offsets[item + 1];
+            if (FW) {
+                fin = a.state_pool + ((int64_t)a.state_indices[item] * H + h) * DK * DV;
+                init = 0;
+                has_v = true;
+            } else {  // slice 0: transition columns M, slice 1: contribution columns U
+                const bool isM = slice == 0;
+                fin = (isM ? a.M : a.U) + ((int64_t)item * H + h) * DK * DV;
+                init = isM ? 1 : 2;
+                has_v = !isM;
+            }
+        } else {
+            if (t == 0) s_next = atomicAdd((int *)&a.plan->ctr[xcd], 1);
+            __syncthreads();
+            // every value of the unit is wave-uniform: keep it in scalar registers
+            const int u = __builtin_amdgcn_readfirstlane(s_next);
+            __syncthreads();
+            if (u >= a.plan->qlen[xcd]) break;
+            const int2 qe = a.queue[xcd * a.qcap + u];
+            const int qx = __builtin_amdgcn_readfirstlane(qe.x), qy = __builtin_amdgcn_readfirstlane(qe.y);
+            if (qy < 0) continue;  // skip slot
+            const int4 en = a.ent[qx];
+            const int seq = __builtin_amdgcn_readfirstlane(en.x), cbeg = __builtin_amdgcn_readfirstlane(en.y);
+            const int cend = __builtin_amdgcn_readfirstlane(en.z), piece = __builtin_amdgcn_readfirstlane(en.w);
+            h = qy & 0xffff;
+            const int role = qy >> 16;
+            const int sb = a.offsets[seq], se = a.offsets[seq + 1];
+            t_begin = sb + 64 * cbeg;
+            t_end = min(se, sb + 64 * cend);
+            if (role == ROLE_WHOLE) {
+                fin = a.state_pool + ((int64_t)a.state_indices[seq] * H + h) * DK * DV;
+                init = 0;
+                has_v = true;
+            } else if (role == ROLE_M) {
+                fin = a.ws_M + ((int64_t)piece * H + h) * DK * DV;
+                init = 1;
+                has_v = false;
+                obase = (bf16_t *)a.ws_W;
+            } else {
+                fin = a.ws_U + ((int64_t)piece * H + h) * DK * DV;
+                init = 2;
+                has_v = true;
+            }
+        }
+        const int len = t_end - t_begin;
+        if (FW && len <= 0) continue;
+        const int n_chunks = len > 0 ? (len + 63) / 64 : 0;
+        const float negA = -expf(a.a_log[h]);
+        const f32x4 dtb = *(const f32x4 *)(a.dt_bias + h * DK + c0) * 1.44269504088896341f;
+
+    // ---- state tile of wave w: rows 16ct+4g+s, column 16w + li
+    // Lane (g, li) holds key rows key_row(ct, 4g + s) = 8g + (32(ct/2) + 4(ct%2) + s): one
+    // lane pointer per unit plus compile-time row offsets.
+    f32x4 S[8];
+    const float *sp = fin + 8 * g * DV + 16 * w + li;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int rr = 32 * (ct >> 1) + 4 * (ct & 1) + s;
+            S[ct][s] = init == 0 ? sp[rr * DV] : ((init == 1 && 8 * g + rr == 16 * w + li) ? 1.f : 0.f);
+        }
 
     // ---- prefetch registers: 4 rows x 4 channels of raw/k/q/v, one beta logit
     f32x4 praw[4];
     bf16x4 pk[4], pq[4], pv[4];
     float pbl = 0.f;
+    if (!has_v)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[r] = bf16x4{};
     // Loads of chunk ck in six small groups (q = 0..5).  Issued a few at a time across
     // the previous chunk's compute, they never fill the memory request queue at once,
     // so the waves issuing them are not held up while every workgroup's loads drain.
@@ -234,11 +284,11 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 pq[2] = *(const bf16x4 *)((const bf16_t *)a.q + row_of(2) * DK + c0);
                 pq[3] = *(const bf16x4 *)((const bf16_t *)a.q + row_of(3) * DK + c0);
             }
-            if (has_v) pv[0] = *(const bf16x4 *)((const bf16_t *)a.v + row_of(0) * DV + col0 + c0);
+            if (has_v) pv[0] = *(const bf16x4 *)((const bf16_t *)a.v + row_of(0) * DV + c0);
         } else {
             if (has_v)
 #pragma unroll
-                for (int r = 1; r < 4; ++r) pv[r] = *(const bf16x4 *)((const bf16_t *)a.v + row_of(r) * DV + col0 + c0);
+                for (int r = 1; r < 4; ++r) pv[r] = *(const bf16x4 *)((const bf16_t *)a.v + row_of(r) * DV + c0);
         }
     };
     if (n_chunks > 0)
@@ -323,7 +373,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             for (int cc = 0; cc < 4; ++cc) {
                 bf16x4 v4;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v4[r] = has_v ? pv[r][cc] : (bf16_t)0.f;
+                for (int r = 0; r < 4; ++r) v4[r] = pv[r][cc];
                 *(bf16x4 *)(sVT + (c0 + cc) * PJ + rbase) = v4;
             }
             if (t < 64) sBeta[t] = (t < n) ? (a.beta_mode == 0 ? 1.f / (1.f + __expf(-pbl)) : pbl) : 0.f;
@@ -479,7 +529,6 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             }
             if (more) issue(ck + 1, 4);
             if (FW) {
-                bf16_t *outp = (bf16_t *)a.out;
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     // O^T += U^T P^T
@@ -490,7 +539,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                     // lane holds O[token 16rt + li][columns 16w + 4g .. +3]: one 8-byte store
                     const int i = 16 * rt + li;
                     if (i < n)
-                        *(bf16x4 *)(outp + ((int64_t)(t0 + i) * H + h) * DV + col0 + 16 * w + 4 * g) =
+                        *(bf16x4 *)(obase + ((int64_t)(t0 + i) * H + h) * DV + 16 * w + 4 * g) =
                             bf4(a.scale * Z[rt]);
                 }
             }
@@ -512,20 +561,13 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
 
     // ---- final state of this tile
     {
-        const int col = col0 + 16 * w + li;
+        float *fp = fin + 8 * g * DV + 16 * w + li;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int r = key_row(ct, 4 * g + s);
-                if (FW)
-                    a.state_pool[(((int64_t)slot * H + h) * DK + r) * DV + col] = S[ct][s];
-                else if (isM)
-                    a.M[(((int64_t)item * H + h) * DK + r) * DK + col] = S[ct][s];
-                else
-                    a.U[(((int64_t)item * H + h) * DK + r) * DV + col] = S[ct][s];
-            }
+            for (int s = 0; s < 4; ++s) fp[(32 * (ct >> 1) + 4 * (ct & 1) + s) * DV] = S[ct][s];
     }
+    }  // units
 }
 
 }  // namespace fast
@@ -537,6 +579,13 @@ hipError_t launch_fast(const ChainArgs &a, int mode, hipStream_t stream) {
         hipLaunchKernelGGL(fast::kda_fast_kernel<MODE_FWD>, grid, dim3(fast::NT), 0, stream, a);
     else
         hipLaunchKernelGGL(fast::kda_fast_kernel<MODE_SUMMARY>, grid, dim3(fast::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fast_planned(const ChainArgs &a, int n_cu, hipStream_t stream) {
+    // persistent: one workgroup per CU (LDS allows no second one), drained queues end it
+    const dim3 grid(8 * ((n_cu + 7) / 8));
+    hipLaunchKernelGGL(fast::kda_fast_kernel<MODE_FWD>, grid, dim3(fast::NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -8,6 +8,34 @@ namespace kda {
 
 enum { MODE_FWD = 0, MODE_SUMMARY = 1 };
 
+// ---- load-balanced forward pass (kda_plan.hip)
+// Roles of a queued unit: the whole sequence or its first piece (state from and to the
+// pool slot, V, outputs to out); the transition chain of a later piece (state starts at
+// I, no V, outputs W_t = scale q_t^T M_t to the W buffer, final M to the M buffer); the
+// contribution chain of a later piece (state starts at 0, V, outputs to out, final U).
+enum { ROLE_WHOLE = 0, ROLE_M = 1, ROLE_U = 2 };
+
+struct PlanHeader {
+    int ctr[8];    // per-XCD queue cursors (atomics), zeroed by the planner
+    int qlen[8];   // per-XCD queue lengths, counting skip slots
+    int n_split;   // sequences cut into pieces
+    int n_piece;   // pieces after the first, over all split sequences
+    int n_echunk;  // chunks in those pieces
+    int L;         // first-piece length in chunks (0: nothing split)
+    int n_ent;
+    int n_sorted;
+    int pad[14];
+};
+
+// Byte offsets of the parts of the forward-pass workspace.
+struct PlanLayout {
+    size_t hdr, queue, ent, piece, sseq, sorted, M, U, IN, W, total;
+    int np_cap;   // capacity for pieces after the first
+    int ent_cap;  // capacity for entities (sequences + pieces)
+    int qcap;     // capacity of one XCD queue (int2 entries)
+};
+PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_cu);
+
 struct ChainArgs {
     const void *q;                // [T,H,dk] (FWD only)
     const void *k;                // [T,H,dk]
@@ -29,6 +57,15 @@ struct ChainArgs {
     float lb;
     int beta_mode;
     float scale;
+    // load-balanced forward pass: when plan is set, workgroups take units from the
+    // per-XCD queues instead of one (item, head) each
+    const PlanHeader *plan;
+    const int2 *queue;       // [8][qcap]: (entity, head | role << 16), head < 0 in skip slots
+    const int4 *ent;         // entity: (sequence, first chunk, end chunk, piece or -1)
+    int qcap;
+    float *ws_M;             // [n_piece][H][dk][dk]
+    float *ws_U;             // [n_piece][H][dk][dv]
+    void *ws_W;              // [T][H][dv] bf16, W rows of the later pieces
 };
 
 // dvs: value columns per workgroup (64 or 128); precise: fp32 inputs.
@@ -38,6 +75,12 @@ hipError_t launch_chain(const ChainArgs &a, int dk, int dvs, bool precise, int m
 // for the forward pass (n_slices = 1) and two (transition / contribution columns) for
 // segment summaries (n_slices = 2).
 hipError_t launch_fast(const ChainArgs &a, int mode, hipStream_t stream);
+// forward pass over the queues of a plan (a.plan set), one persistent workgroup per CU
+hipError_t launch_fast_planned(const ChainArgs &a, int n_cu, hipStream_t stream);
+
+// Planner, piece-state scan and output correction of the load-balanced forward pass
+// (bf16, dk = dv = 128).  ws is the workspace laid out by plan_layout.
+hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int n_cu, hipStream_t stream);
 
 hipError_t launch_affine_scan(int n_seg, int H, int dk, int dv, const float *M, const float *U,
                               const float *S_init, float *incoming, float *outgoing, float *final_state,

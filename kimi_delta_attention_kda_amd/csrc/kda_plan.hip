@@ -1,0 +1,470 @@
+// kda_plan.hip -- load-balanced forward pass: long sequences are cut into pieces that
+// run in parallel (bf16, dk = dv = 128).
+//
+// A (sequence, head) chain is sequential, so one long sequence would bound the kernel
+// while short ones leave their CUs idle.  The context-parallel construction of the "KDA
+// Context Parallelism" page (Theory; Incoming and outgoing states) applies inside one
+// GPU as well: a piece started from state X has S_t = M_t X + U_t, where M_t is the
+// piece's transition up to token t (the chain started from I with no values) and U_t
+// its contribution (the chain started from 0).  Hence
+//     o_t = scale q_t^T S_t = (scale q_t^T M_t) X + scale q_t^T U_t = W_t X + O_U,t,
+// and both chains run without knowing X.  Per forward call:
+//   1. plan_kernel (one workgroup) chooses a first-piece length L, cuts every sequence
+//      longer than 9L/8 into a first piece of L chunks plus near-equal later pieces of at
+//      most L chunks, and deals the units, longest first, into eight per-XCD queues (the
+//      two chains of a later piece next to each other, so they share the XCD's L2);
+//   2. kda_fast_kernel drains the queues: whole sequences and first pieces run from the
+//      pool slot as usual; a later piece runs its transition chain (W_t rows into the W
+//      buffer, final M) and its contribution chain (O_U rows into out, final U);
+//   3. piece_scan_kernel walks each split sequence's pieces in order: the incoming
+//      state of a piece is X_k, X_{k+1} = M_k X_k + U_k, the last one goes to the slot;
+//   4. fixup_kernel adds W_t X_k to the outputs of every later piece.
+// L is the smallest length for which the total work (a later piece costs two chains)
+// spread over all CUs fits in L chunks and the units longer than L/2 (no two of which
+// fit on one CU within L) are no more than the CUs, so the makespan stays near L.
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace plan {
+
+constexpr int PT = 1024;   // planner threads
+constexpr int NBIN = 1024; // length bins of the longest-first order
+constexpr int L_MIN = 4;   // shortest first piece worth a split, in chunks
+constexpr int DK = 128, DV = 128;
+
+static_assert(NBIN == PT, "one bin per planner thread");
+
+struct PlanArgs {
+    const int32_t *cu;
+    int B, H, n_cu;
+    PlanHeader *hdr;
+    int2 *queue;
+    int4 *ent;
+    int4 *piece;   // (sequence, first chunk, end chunk, prefix of later-piece chunks)
+    int4 *sseq;    // (sequence, first later piece, number of later pieces, 0)
+    int *sorted;
+    int np_cap, ent_cap, qcap;
+};
+
+__device__ __forceinline__ int chunks_of(const int32_t *cu, int b) {
+    const int len = cu[b + 1] - cu[b];
+    return len > 0 ? (len + 63) / 64 : 0;
+}
+
+// Sum / max over the workgroup; every thread gets the result.
+__device__ int64_t block_sum(int64_t v, int64_t *red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int64_t s = 0;
+#pragma unroll
+    for (int i = 0; i < PT / 64; ++i) s += red[i];
+    return s;
+}
+__device__ int block_max(int v, int64_t *red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int m = 0;
+#pragma unroll
+    for (int i = 0; i < PT / 64; ++i) m = max(m, (int)red[i]);
+    return m;
+}
+// Exclusive prefix sum over the threads of the workgroup; total returned in *tot.
+__device__ int block_excl_scan(int v, int64_t *red, int *tot) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) red[wv] = x;
+    __syncthreads();
+    int base = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < PT / 64; ++i) {
+        const int r = (int)red[i];
+        if (i < wv) base += r;
+        all += r;
+    }
+    *tot = all;
+    return base + x - v;
+}
+
+__global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
+    __shared__ int64_t red[PT / 64];
+    __shared__ int hist[NBIN];
+    const int t = threadIdx.x;
+    const int B = p.B, H = p.H;
+
+    // ---- chunk totals
+    int64_t s_loc = 0;
+    int m_loc = 0;
+    for (int b = t; b < B; b += PT) {
+        const int n = chunks_of(p.cu, b);
+        s_loc += n;
+        m_loc = max(m_loc, n);
+    }
+    const int64_t S = block_sum(s_loc, red);
+    const int maxn = block_max(m_loc, red);
+
+    // ---- first-piece length: smallest L >= average load with H (S + E(L)) <= n_cu L,
+    // E(L) = chunks moved into later pieces (they run twice)
+    const int64_t L0 = max((int64_t)L_MIN, ((int64_t)H * S + p.n_cu - 1) / p.n_cu);
+    int L = 0;
+    if (8 * (int64_t)maxn > 9 * L0) {
+        int lo = (int)L0, hi = maxn;
+        while (lo < hi) {  // uniform: every thread sees the same sums
+            const int mid = lo + (hi - lo) / 2;
+            int64_t e = 0;
+            for (int b = t; b < B; b += PT) {
+                const int n = chunks_of(p.cu, b);
+                if (8 * (int64_t)n > 9 * (int64_t)mid) e += n - mid;
+            }
+            const int64_t E = block_sum(e, red);
+            if ((int64_t)H * (S + E) <= (int64_t)p.n_cu * mid) hi = mid;
+            else lo = mid + 1;
+        }
+        L = lo;
+        // Units longer than L/2 cannot share a CU within about L: while they outnumber
+        // the CUs, lengthen the pieces (fewer, longer units).
+        while (L < maxn) {
+            int64_t big = 0;
+            for (int b = t; b < B; b += PT) {
+                const int n = chunks_of(p.cu, b);
+                if (8 * (int64_t)n > 9 * (int64_t)L) {
+                    const int R = n - L, P = (R + L - 1) / L, base = R / P, rem = R % P;
+                    big += 1 + 2 * ((2 * (base + 1) > L ? rem : 0) + (2 * base > L ? P - rem : 0));
+                } else if (2 * n > L) {
+                    big += 1;
+                }
+            }
+            if ((int64_t)H * block_sum(big, red) <= p.n_cu) break;
+            L = max(L + 1, (int)((int64_t)L * 17 / 16));
+        }
+        if (!(8 * (int64_t)maxn > 9 * (int64_t)L)) L = 0;
+    }
+
+    // ---- pieces: each thread owns a contiguous range of sequences, so the later
+    // pieces of one sequence get consecutive indices
+    const int per = (B + PT - 1) / PT;
+    const int b0 = min(B, t * per), b1 = min(B, b0 + per);
+    int my_p = 0, my_s = 0, my_e = 0;
+    auto split_of = [&](int n) { return L > 0 && 8 * (int64_t)n > 9 * (int64_t)L; };
+    for (int b = b0; b < b1; ++b) {
+        const int n = chunks_of(p.cu, b);
+        if (split_of(n)) {
+            my_p += (n - L + L - 1) / L;
+            my_s += 1;
+            my_e += n - L;
+        }
+    }
+    int tot_p, tot_s, tot_e;
+    int kb = block_excl_scan(my_p, red, &tot_p);
+    int jb = block_excl_scan(my_s, red, &tot_s);
+    int eb = block_excl_scan(my_e, red, &tot_e);
+    if (tot_p > p.np_cap || B + tot_p > p.ent_cap) {  // cannot happen by the sizing; stay safe
+        L = 0;
+        tot_p = tot_s = tot_e = 0;
+    }
+    for (int b = b0; b < b1; ++b) {
+        const int n = chunks_of(p.cu, b);
+        if (split_of(n)) {
+            const int R = n - L, P = (R + L - 1) / L, base = R / P, rem = R % P;
+            p.sseq[jb] = make_int4(b, kb, P, 0);
+            int c = L;
+            for (int i = 0; i < P; ++i) {
+                const int len = base + (i < rem ? 1 : 0);
+                p.piece[kb + i] = make_int4(b, c, c + len, eb);
+                p.ent[B + kb + i] = make_int4(b, c, c + len, kb + i);
+                c += len;
+                eb += len;
+            }
+            p.ent[b] = make_int4(b, 0, L, -1);
+            kb += P;
+            jb += 1;
+        } else {
+            p.ent[b] = make_int4(b, 0, n, -1);
+        }
+    }
+    const int n_ent = B + tot_p;
+    __syncthreads();
+
+    // ---- longest first: counting sort of the entities on 1024 length bins
+    int ml = 0;
+    for (int e = t; e < n_ent; e += PT) ml = max(ml, p.ent[e].z - p.ent[e].y);
+    const int maxlen = max(1, block_max(ml, red));
+    hist[t] = 0;
+    __syncthreads();
+    for (int e = t; e < n_ent; e += PT) {
+        const int len = p.ent[e].z - p.ent[e].y;
+        if (len > 0) atomicAdd(&hist[NBIN - 1 - (int)((int64_t)len * (NBIN - 1) / maxlen)], 1);
+    }
+    __syncthreads();
+    int n_sorted;
+    const int start = block_excl_scan(hist[t], red, &n_sorted);
+    __syncthreads();
+    hist[t] = start;
+    __syncthreads();
+    for (int e = t; e < n_ent; e += PT) {
+        const int len = p.ent[e].z - p.ent[e].y;
+        if (len > 0) {
+            const int pos = atomicAdd(&hist[NBIN - 1 - (int)((int64_t)len * (NBIN - 1) / maxlen)], 1);
+            p.sorted[pos] = e;
+        }
+    }
+    __syncthreads();
+
+    // ---- per-XCD queues: super unit s = (rank, head) goes to XCD s % 8, slots 2(s/8) and
+    // 2(s/8) + 1 (the contribution chain of a later piece, else a skip slot)
+    const int64_t NS = (int64_t)n_sorted * H;
+    for (int64_t s = t; s < NS; s += PT) {
+        const int r = (int)(s / H), hh = (int)(s - (int64_t)r * H);
+        const int e = p.sorted[r];
+        const bool pair = p.ent[e].w >= 0;
+        const int x = (int)(s & 7);
+        const int64_t i = s >> 3;
+        int2 *q = p.queue + (int64_t)x * p.qcap + 2 * i;
+        q[0] = make_int2(e, hh | ((pair ? ROLE_M : ROLE_WHOLE) << 16));
+        q[1] = pair ? make_int2(e, hh | (ROLE_U << 16)) : make_int2(0, -1);
+    }
+    if (t < 8) {
+        p.hdr->ctr[t] = 0;
+        p.hdr->qlen[t] = NS > t ? (int)(2 * ((NS - t + 7) / 8)) : 0;
+    }
+    if (t == 0) {
+        p.hdr->n_split = tot_s;
+        p.hdr->n_piece = tot_p;
+        p.hdr->n_echunk = tot_e;
+        p.hdr->L = L;
+        p.hdr->n_ent = n_ent;
+        p.hdr->n_sorted = n_sorted;
+    }
+}
+
+struct PieceArgs {
+    const PlanHeader *hdr;
+    const int4 *piece, *sseq;
+    const int32_t *cu;
+    const int32_t *state_indices;
+    float *state_pool;
+    const float *M, *U;
+    float *IN;
+    const bf16_t *W;
+    bf16_t *out;
+    int H;
+};
+
+// Incoming states of the later pieces, in order, and the final state into the slot.
+// Task = (split sequence, head, 16-column block); thread t owns row t/2, 8 columns.
+__global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
+    __shared__ float sx[DK][16];
+    const int t = threadIdx.x, H = p.H;
+    const int r = t >> 1, half = t & 1;
+    const int n_tasks = p.hdr->n_split * H * (DV / 16);
+    for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
+        const int cb = task & 7, jh = task >> 3;
+        const int h = jh % H, j = jh / H;
+        const int4 sq = p.sseq[j];
+        const int c0 = 16 * cb + 8 * half;
+        float *slot = p.state_pool + ((int64_t)p.state_indices[sq.x] * H + h) * DK * DV;
+        float x[8];
+        {
+            const f32x4 a0 = *(const f32x4 *)(slot + r * DV + c0), a1 = *(const f32x4 *)(slot + r * DV + c0 + 4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                x[c] = a0[c];
+                x[c + 4] = a1[c];
+            }
+        }
+        for (int i = 0; i < sq.z; ++i) {
+            const int64_t kh = (int64_t)(sq.y + i) * H + h;
+            float *inw = p.IN + kh * DK * DV + r * DV + c0;
+            *(f32x4 *)inw = f32x4{x[0], x[1], x[2], x[3]};
+            *(f32x4 *)(inw + 4) = f32x4{x[4], x[5], x[6], x[7]};
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sx[r][8 * half + c] = x[c];
+            __syncthreads();
+            const float *Mr = p.M + kh * DK * DK + r * DK;
+            const float *Ur = p.U + kh * DK * DV + r * DV + c0;
+            const f32x4 u0 = *(const f32x4 *)Ur, u1 = *(const f32x4 *)(Ur + 4);
+            float y[8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                y[c] = u0[c];
+                y[c + 4] = u1[c];
+            }
+            // X_{k+1} = M_k X_k + U_k, fp32, keys in order
+            for (int k0 = 0; k0 < DK; k0 += 4) {
+                const f32x4 m = *(const f32x4 *)(Mr + k0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) y[c] = fmaf(m[q], sx[k0 + q][8 * half + c], y[c]);
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = y[c];
+        }
+        *(f32x4 *)(slot + r * DV + c0) = f32x4{x[0], x[1], x[2], x[3]};
+        *(f32x4 *)(slot + r * DV + c0 + 4) = f32x4{x[4], x[5], x[6], x[7]};
+        __syncthreads();
+    }
+}
+
+// out_t += W_t X_k for every token of every later piece.  Task = (piece, head, chunk),
+// numbered piece-major so that a workgroup's contiguous share of tasks reuses X_k^T,
+// staged once in LDS as bf16.  Wave w computes columns 32w .. 32w+31 as
+// C^T = X^T W^T (16x16x32 bf16 MFMA), so that each lane adds 4 consecutive columns of one
+// token (one 8-byte read-modify-write).
+__global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
+    constexpr int PX = DK + 8;
+    __shared__ __attribute__((aligned(16))) bf16_t sxt[DV * PX];
+    const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
+    const int H = p.H;
+    const int n_piece = p.hdr->n_piece;
+    const int64_t n_tasks = (int64_t)p.hdr->n_echunk * H;
+    const int64_t per = (n_tasks + gridDim.x - 1) / gridDim.x;
+    const int64_t lo_t = (int64_t)blockIdx.x * per, hi_t = min(n_tasks, lo_t + per);
+    int cur = -1;
+    for (int64_t task = lo_t; task < hi_t; ++task) {
+        int lo = 0, hi = n_piece - 1;  // last piece whose task range starts at or before task
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)H * p.piece[mid].w <= task) lo = mid;
+            else hi = mid - 1;
+        }
+        const int4 pc = p.piece[lo];
+        const int len = pc.z - pc.y;
+        const int64_t rem = task - (int64_t)H * pc.w;
+        const int h = (int)(rem / len), c = (int)(rem - (int64_t)h * len);
+        const int key = lo * H + h;
+        if (key != cur) {
+            __syncthreads();
+            const float *X = p.IN + ((int64_t)lo * H + h) * DK * DV;
+            for (int e = t; e < DK * DV / 4; e += 256) {
+                const int kr = e >> 5, c4 = (e & 31) * 4;
+                const f32x4 v = *(const f32x4 *)(X + kr * DV + c4);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sxt[(c4 + q) * PX + kr] = (bf16_t)v[q];
+            }
+            __syncthreads();
+            cur = key;
+        }
+        const int s0 = p.cu[pc.x], s1 = p.cu[pc.x + 1];
+        const int t0 = s0 + 64 * (pc.y + c);
+        const int n = min(64, s1 - t0);
+        for (int tt = 0; tt < 4 && 16 * tt < n; ++tt) {
+            const int row = t0 + min(16 * tt + li, n - 1);
+            const bf16_t *wr = p.W + ((int64_t)row * H + h) * DV;
+            f32x4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const bf16x8 bw = *(const bf16x8 *)(wr + 32 * kb + 8 * g);
+                acc0 = mfma(*(const bf16x8 *)(sxt + (32 * w + li) * PX + 32 * kb + 8 * g), bw, acc0);
+                acc1 = mfma(*(const bf16x8 *)(sxt + (32 * w + 16 + li) * PX + 32 * kb + 8 * g), bw, acc1);
+            }
+            if (16 * tt + li < n) {
+                bf16_t *o = p.out + ((int64_t)(t0 + 16 * tt + li) * H + h) * DV + 32 * w + 4 * g;
+                *(bf16x4 *)o = bf4(f4(*(const bf16x4 *)o) + acc0);
+                *(bf16x4 *)(o + 16) = bf4(f4(*(const bf16x4 *)(o + 16)) + acc1);
+            }
+        }
+    }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace plan
+
+PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_cu) {
+    PlanLayout y;
+    // later pieces per head <= total chunks / L <= n_cu / H (L is at least the average
+    // load); twice that plus slack
+    y.np_cap = 2 * ((n_cu + H - 1) / H) + 2;
+    y.ent_cap = B + y.np_cap;
+    y.qcap = (int)(2 * (((int64_t)y.ent_cap * H + 7) / 8) + 2);
+    size_t o = 0;
+    y.hdr = o;
+    o = plan::align256(o + sizeof(PlanHeader));
+    y.queue = o;
+    o = plan::align256(o + (size_t)8 * y.qcap * sizeof(int2));
+    y.ent = o;
+    o = plan::align256(o + (size_t)y.ent_cap * sizeof(int4));
+    y.piece = o;
+    o = plan::align256(o + (size_t)y.np_cap * sizeof(int4));
+    y.sseq = o;
+    o = plan::align256(o + (size_t)y.np_cap * sizeof(int4));
+    y.sorted = o;
+    o = plan::align256(o + (size_t)y.ent_cap * sizeof(int));
+    const size_t st = (size_t)y.np_cap * H * dk * dv * sizeof(float);
+    y.M = o;
+    o = plan::align256(o + (size_t)y.np_cap * H * dk * dk * sizeof(float));
+    y.U = o;
+    o = plan::align256(o + st);
+    y.IN = o;
+    o = plan::align256(o + st);
+    y.W = o;
+    o = plan::align256(o + (size_t)T * H * dv * sizeof(bf16_t));
+    y.total = o;
+    return y;
+}
+
+hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int n_cu, hipStream_t stream) {
+    plan::PlanArgs pa;
+    pa.cu = a.offsets;
+    pa.B = a.n_items;
+    pa.H = a.H;
+    pa.n_cu = n_cu;
+    pa.hdr = (PlanHeader *)(ws + lay.hdr);
+    pa.queue = (int2 *)(ws + lay.queue);
+    pa.ent = (int4 *)(ws + lay.ent);
+    pa.piece = (int4 *)(ws + lay.piece);
+    pa.sseq = (int4 *)(ws + lay.sseq);
+    pa.sorted = (int *)(ws + lay.sorted);
+    pa.np_cap = lay.np_cap;
+    pa.ent_cap = lay.ent_cap;
+    pa.qcap = lay.qcap;
+    hipLaunchKernelGGL(plan::plan_kernel, dim3(1), dim3(plan::PT), 0, stream, pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    a.plan = pa.hdr;
+    a.queue = pa.queue;
+    a.ent = pa.ent;
+    a.qcap = lay.qcap;
+    a.ws_M = (float *)(ws + lay.M);
+    a.ws_U = (float *)(ws + lay.U);
+    a.ws_W = ws + lay.W;
+    e = launch_fast_planned(a, n_cu, stream);
+    if (e != hipSuccess) return e;
+
+    plan::PieceArgs pp;
+    pp.hdr = pa.hdr;
+    pp.piece = pa.piece;
+    pp.sseq = pa.sseq;
+    pp.cu = a.offsets;
+    pp.state_indices = a.state_indices;
+    pp.state_pool = a.state_pool;
+    pp.M = a.ws_M;
+    pp.U = a.ws_U;
+    pp.IN = (float *)(ws + lay.IN);
+    pp.W = (const bf16_t *)a.ws_W;
+    pp.out = (bf16_t *)a.out;
+    pp.H = a.H;
+    hipLaunchKernelGGL(plan::piece_scan_kernel, dim3(n_cu), dim3(256), 0, stream, pp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(plan::fixup_kernel, dim3(2 * n_cu), dim3(256), 0, stream, pp);
+    return hipGetLastError();
+}
+
+}  // namespace kda

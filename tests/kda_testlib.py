@@ -17,13 +17,14 @@ def gate_name(w):
     return "safe" if w.gate_mode == 1 else "original"
 
 
-def run_fwd(w, inp, pool=None):
+def run_fwd(w, inp, pool=None, workspace="torch"):
     """Runs kda_chunk_fwd on the workload's tensors; returns (out, pool_after)."""
     pool = inp["state_pool"].clone() if pool is None else pool
     out = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["raw_gate"], inp["beta_logits"],
                         inp["a_log"], inp["dt_bias"], inp["cu_seqlens"], pool, inp["state_indices"],
                         gate_mode=gate_name(w), lower_bound=w.lower_bound,
-                        beta_mode="logits" if w.beta_mode == 0 else "probability", scale=w.scale)
+                        beta_mode="logits" if w.beta_mode == 0 else "probability", scale=w.scale,
+                        workspace=workspace)
     torch.cuda.synchronize()
     return out, pool
 

@@ -97,6 +97,38 @@ def test_chunk_fwd_error_paths(L):
     assert _fwd(L, _desc(T=0)) == OK
 
 
+def _fwd_ws(L, d, ws=FAKE, nbytes=1 << 40, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, raw=FAKE, beta=FAKE, a_log=FAKE, dtb=FAKE, cu=FAKE, pool=FAKE,
+             idx=FAKE, out=FAKE)
+    p.update(ptrs)
+    return L.kda_chunk_fwd_ws(C.byref(d) if d is not None else None, p["q"], p["k"], p["v"], p["raw"],
+                              p["beta"], p["a_log"], p["dtb"], p["cu"], p["pool"], p["idx"], p["out"],
+                              ws, nbytes, None)
+
+
+def test_workspace_variant_error_paths(L):
+    # the same validation as kda_chunk_fwd, before the workspace is looked at
+    assert _fwd_ws(L, None) == ENULL
+    assert _fwd_ws(L, _desc(), out=None) == ENULL
+    assert _fwd_ws(L, _desc(T=-1)) == ESHAPE
+    assert _fwd_ws(L, _desc(gate_mode="original")) == EUNSUP
+    assert _fwd_ws(L, _desc(B=0)) == OK
+    n = C.c_size_t(7)
+    assert L.kda_chunk_fwd_workspace_size(None, C.byref(n)) == ENULL
+    assert L.kda_chunk_fwd_workspace_size(C.byref(_desc()), None) == ENULL
+    # f32 and dk = 64 never use the load-balanced pass: no workspace, no device query
+    assert L.kda_chunk_fwd_workspace_size(C.byref(_desc(qkv_dtype=torch.float32, out_dtype=torch.float32,
+                                                         dk=64, dv=64)), C.byref(n)) == OK
+    assert n.value == 0
+    assert L.kda_chunk_fwd_workspace_size(C.byref(_desc(dk=64, dv=64)), C.byref(n)) == OK
+    assert n.value == 0
+    # bf16 dk = dv = 128 sizes for the current device (HIP error without one)
+    st = L.kda_chunk_fwd_workspace_size(C.byref(_desc()), C.byref(n))
+    assert st in (OK, 6)
+    if st == OK:
+        assert n.value >= 128 * 4 * 128 * 2
+
+
 def test_summary_and_scan_error_paths(L):
     d = _desc()
     args = [FAKE] * 7
