@@ -100,7 +100,7 @@ __device__ __forceinline__ void split_h(f32x4 x, f16x4 &hi, f16x4 &lo) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         hi[s] = (f16_t)x[s];
-        lo[s] = (f16_t)(x[s] - (float)hi[s]);
+        lo[s] = (f16_t)fmaf((float)hi[s], -1.f, x[s]);  // x - hi, exact
     }
 }
 
@@ -155,9 +155,10 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     float *sEG = (float *)(smem + L::EG);
 
     const int H = a.H;
-    const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
+    const int t = threadIdx.x, l = t & 63, g = l >> 4, li = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, in a scalar register
     // prep role: block I, key channels c0 .. c0+3, rows 16I + 4rq + [0, 4)
-    const int I = t >> 7, rq = t & 3, c0 = 4 * ((t >> 2) & 31);
+    const int I = __builtin_amdgcn_readfirstlane(t >> 7), rq = t & 3, c0 = 4 * ((t >> 2) & 31);
     const int rbase = 16 * I + 4 * rq;
     const float amin = a.gate_mode == 1 ? expf(a.lb) : 0.f;  // alpha floor of the safe gate
     const int xcd = blockIdx.x & 7;  // workgroups are dealt to the 8 XCDs round-robin
@@ -259,36 +260,47 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     // Loads of chunk ck in six small groups (q = 0..5).  Issued a few at a time across
     // the previous chunk's compute, they never fill the memory request queue at once,
     // so the waves issuing them are not held up while every workgroup's loads drain.
+    // Addresses: a scalar base per chunk (its first token, this head) plus 32-bit lane
+    // offsets; the four row offsets of a chunk are formed once, at its first group.
+    unsigned roff[4];
     auto issue = [&](int ck, int q) {
         const int t0 = t_begin + ck * 64;
-        const int n = min(64, t_end - t0);
-        auto row_of = [&](int r) { return ((int64_t)(t0 + min(rbase + r, n - 1)) * H + h); };
+        const int64_t rb = (int64_t)t0 * H + h;
         if (q == 0) {
-            praw[0] = *(const f32x4 *)(a.raw_gate + row_of(0) * DK + c0);
-            praw[1] = *(const f32x4 *)(a.raw_gate + row_of(1) * DK + c0);
+            const int n = min(64, t_end - t0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) roff[r] = (unsigned)(min(rbase + r, n - 1) * (H * DK) + c0);
+        }
+        const float *rg = a.raw_gate + rb * DK;
+        const bf16_t *kp = (const bf16_t *)a.k + rb * DK;
+        const bf16_t *qp = (const bf16_t *)a.q + rb * DK;
+        const bf16_t *vp = (const bf16_t *)a.v + rb * DV;
+        if (q == 0) {
+            praw[0] = *(const f32x4 *)(rg + roff[0]);
+            praw[1] = *(const f32x4 *)(rg + roff[1]);
         } else if (q == 1) {
-            praw[2] = *(const f32x4 *)(a.raw_gate + row_of(2) * DK + c0);
-            praw[3] = *(const f32x4 *)(a.raw_gate + row_of(3) * DK + c0);
-            if (t < 64) pbl = a.beta_logits[(int64_t)(t0 + min(t, n - 1)) * H + h];
+            praw[2] = *(const f32x4 *)(rg + roff[2]);
+            praw[3] = *(const f32x4 *)(rg + roff[3]);
+            if (t < 64) pbl = a.beta_logits[rb + (unsigned)(min(t, t_end - t0 - 1) * H)];
         } else if (q == 2) {
 #pragma unroll
-            for (int r = 0; r < 3; ++r) pk[r] = *(const bf16x4 *)((const bf16_t *)a.k + row_of(r) * DK + c0);
+            for (int r = 0; r < 3; ++r) pk[r] = *(const bf16x4 *)(kp + roff[r]);
         } else if (q == 3) {
-            pk[3] = *(const bf16x4 *)((const bf16_t *)a.k + row_of(3) * DK + c0);
+            pk[3] = *(const bf16x4 *)(kp + roff[3]);
             if (FW) {
-                pq[0] = *(const bf16x4 *)((const bf16_t *)a.q + row_of(0) * DK + c0);
-                pq[1] = *(const bf16x4 *)((const bf16_t *)a.q + row_of(1) * DK + c0);
+                pq[0] = *(const bf16x4 *)(qp + roff[0]);
+                pq[1] = *(const bf16x4 *)(qp + roff[1]);
             }
         } else if (q == 4) {
             if (FW) {
-                pq[2] = *(const bf16x4 *)((const bf16_t *)a.q + row_of(2) * DK + c0);
-                pq[3] = *(const bf16x4 *)((const bf16_t *)a.q + row_of(3) * DK + c0);
+                pq[2] = *(const bf16x4 *)(qp + roff[2]);
+                pq[3] = *(const bf16x4 *)(qp + roff[3]);
             }
-            if (has_v) pv[0] = *(const bf16x4 *)((const bf16_t *)a.v + row_of(0) * DV + c0);
+            if (has_v) pv[0] = *(const bf16x4 *)(vp + roff[0]);
         } else {
             if (has_v)
 #pragma unroll
-                for (int r = 1; r < 4; ++r) pv[r] = *(const bf16x4 *)((const bf16_t *)a.v + row_of(r) * DV + c0);
+                for (int r = 1; r < 4; ++r) pv[r] = *(const bf16x4 *)(vp + roff[r]);
         }
     };
     if (n_chunks > 0)
@@ -367,7 +379,8 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             if (rq == 0) {
                 *(f32x4 *)(sE + I * DK + c0) = E;
                 // 1/E <= e^{16 |bound|}: finite under the safe gate
-                *(f32x4 *)(sIE + I * DK + c0) = f32x4{1.f / E[0], 1.f / E[1], 1.f / E[2], 1.f / E[3]};
+                *(f32x4 *)(sIE + I * DK + c0) = f32x4{__builtin_amdgcn_rcpf(E[0]), __builtin_amdgcn_rcpf(E[1]),
+                                                     __builtin_amdgcn_rcpf(E[2]), __builtin_amdgcn_rcpf(E[3])};
             }
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
@@ -431,24 +444,27 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                     const bf16x8 aK = *(const bf16x8 *)(sKR + (16 * bI + li) * PK + cc);
                     const bf16x8 kcv = *(const bf16x8 *)(sKC + (16 * bJ + li) * PK + cc);
                     // e^{G_(16I-1) - G_(16J+15)}: 1/E_I on the diagonal, else the product of
-                    // the decays of the whole blocks strictly between J and I (at most two)
-                    f32x4 m0, m1;
-                    if (bI == bJ) {
-                        m0 = *(const f32x4 *)(sIE + bI * DK + cc);
-                        m1 = *(const f32x4 *)(sIE + bI * DK + cc + 4);
-                    } else {
-                        m0 = f32x4{1.f, 1.f, 1.f, 1.f};
-                        m1 = m0;
-                        for (int K = bJ + 1; K < bI; ++K) {
-                            m0 *= *(const f32x4 *)(sE + K * DK + cc);
-                            m1 *= *(const f32x4 *)(sE + K * DK + cc + 4);
+                    // the decays of the whole blocks strictly between J and I (at most two);
+                    // adjacent blocks have none, factor 1 (the pair is wave-uniform)
+                    bf16x8 bK = kcv;
+                    if (bI != bJ + 1) {
+                        f32x4 m0, m1;
+                        if (bI == bJ) {
+                            m0 = *(const f32x4 *)(sIE + bI * DK + cc);
+                            m1 = *(const f32x4 *)(sIE + bI * DK + cc + 4);
+                        } else {
+                            m0 = *(const f32x4 *)(sE + (bJ + 1) * DK + cc);
+                            m1 = *(const f32x4 *)(sE + (bJ + 1) * DK + cc + 4);
+                            if (bI == bJ + 3) {
+                                m0 *= *(const f32x4 *)(sE + (bJ + 2) * DK + cc);
+                                m1 *= *(const f32x4 *)(sE + (bJ + 2) * DK + cc + 4);
+                            }
                         }
-                    }
-                    bf16x8 bK;
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        bK[s] = (bf16_t)((float)kcv[s] * m0[s]);
-                        bK[s + 4] = (bf16_t)((float)kcv[s + 4] * m1[s]);
+                        for (int s = 0; s < 4; ++s) {
+                            bK[s] = (bf16_t)((float)kcv[s] * m0[s]);
+                            bK[s + 4] = (bf16_t)((float)kcv[s + 4] * m1[s]);
+                        }
                     }
                     accA = mfma(aK, bK, accA);
                     if (FW) accP = mfma(*(const bf16x8 *)(sQR + (16 * bI + li) * PK + cc), bK, accP);
@@ -539,7 +555,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                     // lane holds O[token 16rt + li][columns 16w + 4g .. +3]: one 8-byte store
                     const int i = 16 * rt + li;
                     if (i < n)
-                        *(bf16x4 *)(obase + ((int64_t)(t0 + i) * H + h) * DV + 16 * w + 4 * g) =
+                        *(bf16x4 *)(obase + ((int64_t)t0 * H + h) * DV + (unsigned)(i * (H * DV) + 16 * w + 4 * g)) =
                             bf4(a.scale * Z[rt]);
                 }
             }

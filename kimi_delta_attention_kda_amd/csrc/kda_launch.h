@@ -29,7 +29,7 @@ struct PlanHeader {
 
 // Byte offsets of the parts of the forward-pass workspace.
 struct PlanLayout {
-    size_t hdr, queue, ent, piece, sseq, sorted, M, U, IN, W, total;
+    size_t hdr, queue, ent, piece, sseq, sorted, M, U, XT, W, total;
     int np_cap;   // capacity for pieces after the first
     int ent_cap;  // capacity for entities (sequences + pieces)
     int qcap;     // capacity of one XCD queue (int2 entries)

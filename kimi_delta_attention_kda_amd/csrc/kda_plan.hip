@@ -32,6 +32,8 @@ namespace plan {
 constexpr int PT = 1024;   // planner threads
 constexpr int NBIN = 1024; // length bins of the longest-first order
 constexpr int L_MIN = 4;   // shortest first piece worth a split, in chunks
+constexpr int NCACHE = 4096;  // sequences whose chunk counts the planner keeps in LDS
+constexpr int ECACHE = 1024;  // entities the planner keeps in LDS
 constexpr int DK = 128, DV = 128;
 
 static_assert(NBIN == PT, "one bin per planner thread");
@@ -102,14 +104,22 @@ __device__ int block_excl_scan(int v, int64_t *red, int *tot) {
 __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
     __shared__ int64_t red[PT / 64];
     __shared__ int hist[NBIN];
+    __shared__ int sn[NCACHE];
+    __shared__ int4 sent[ECACHE];
+    __shared__ int ssort[ECACHE];
     const int t = threadIdx.x;
     const int B = p.B, H = p.H;
+    const bool cached = B <= NCACHE;
+    if (cached)
+        for (int b = t; b < B; b += PT) sn[b] = chunks_of(p.cu, b);
+    __syncthreads();
+    auto chunks = [&](int b) { return cached ? sn[b] : chunks_of(p.cu, b); };
 
     // ---- chunk totals
     int64_t s_loc = 0;
     int m_loc = 0;
     for (int b = t; b < B; b += PT) {
-        const int n = chunks_of(p.cu, b);
+        const int n = chunks(b);
         s_loc += n;
         m_loc = max(m_loc, n);
     }
@@ -126,7 +136,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
             const int mid = lo + (hi - lo) / 2;
             int64_t e = 0;
             for (int b = t; b < B; b += PT) {
-                const int n = chunks_of(p.cu, b);
+                const int n = chunks(b);
                 if (8 * (int64_t)n > 9 * (int64_t)mid) e += n - mid;
             }
             const int64_t E = block_sum(e, red);
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
         while (L < maxn) {
             int64_t big = 0;
             for (int b = t; b < B; b += PT) {
-                const int n = chunks_of(p.cu, b);
+                const int n = chunks(b);
                 if (8 * (int64_t)n > 9 * (int64_t)L) {
                     const int R = n - L, P = (R + L - 1) / L, base = R / P, rem = R % P;
                     big += 1 + 2 * ((2 * (base + 1) > L ? rem : 0) + (2 * base > L ? P - rem : 0));
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
     int my_p = 0, my_s = 0, my_e = 0;
     auto split_of = [&](int n) { return L > 0 && 8 * (int64_t)n > 9 * (int64_t)L; };
     for (int b = b0; b < b1; ++b) {
-        const int n = chunks_of(p.cu, b);
+        const int n = chunks(b);
         if (split_of(n)) {
             my_p += (n - L + L - 1) / L;
             my_s += 1;
@@ -175,8 +185,15 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
         L = 0;
         tot_p = tot_s = tot_e = 0;
     }
+    const int n_ent = B + tot_p;
+    const bool ecached = n_ent <= ECACHE;
+    auto put_ent = [&](int e, int4 v) {
+        p.ent[e] = v;
+        if (ecached) sent[e] = v;
+    };
+    auto ent_at = [&](int e) { return ecached ? sent[e] : p.ent[e]; };
     for (int b = b0; b < b1; ++b) {
-        const int n = chunks_of(p.cu, b);
+        const int n = chunks(b);
         if (split_of(n)) {
             const int R = n - L, P = (R + L - 1) / L, base = R / P, rem = R % P;
             p.sseq[jb] = make_int4(b, kb, P, 0);
@@ -184,28 +201,31 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
             for (int i = 0; i < P; ++i) {
                 const int len = base + (i < rem ? 1 : 0);
                 p.piece[kb + i] = make_int4(b, c, c + len, eb);
-                p.ent[B + kb + i] = make_int4(b, c, c + len, kb + i);
+                put_ent(B + kb + i, make_int4(b, c, c + len, kb + i));
                 c += len;
                 eb += len;
             }
-            p.ent[b] = make_int4(b, 0, L, -1);
+            put_ent(b, make_int4(b, 0, L, -1));
             kb += P;
             jb += 1;
         } else {
-            p.ent[b] = make_int4(b, 0, n, -1);
+            put_ent(b, make_int4(b, 0, n, -1));
         }
     }
-    const int n_ent = B + tot_p;
     __syncthreads();
 
     // ---- longest first: counting sort of the entities on 1024 length bins
     int ml = 0;
-    for (int e = t; e < n_ent; e += PT) ml = max(ml, p.ent[e].z - p.ent[e].y);
+    for (int e = t; e < n_ent; e += PT) {
+        const int4 en = ent_at(e);
+        ml = max(ml, en.z - en.y);
+    }
     const int maxlen = max(1, block_max(ml, red));
     hist[t] = 0;
     __syncthreads();
     for (int e = t; e < n_ent; e += PT) {
-        const int len = p.ent[e].z - p.ent[e].y;
+        const int4 en = ent_at(e);
+        const int len = en.z - en.y;
         if (len > 0) atomicAdd(&hist[NBIN - 1 - (int)((int64_t)len * (NBIN - 1) / maxlen)], 1);
     }
     __syncthreads();
@@ -215,10 +235,12 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
     hist[t] = start;
     __syncthreads();
     for (int e = t; e < n_ent; e += PT) {
-        const int len = p.ent[e].z - p.ent[e].y;
+        const int4 en = ent_at(e);
+        const int len = en.z - en.y;
         if (len > 0) {
             const int pos = atomicAdd(&hist[NBIN - 1 - (int)((int64_t)len * (NBIN - 1) / maxlen)], 1);
-            p.sorted[pos] = e;
+            if (ecached) ssort[pos] = e;
+            else p.sorted[pos] = e;
         }
     }
     __syncthreads();
@@ -228,8 +250,8 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
     const int64_t NS = (int64_t)n_sorted * H;
     for (int64_t s = t; s < NS; s += PT) {
         const int r = (int)(s / H), hh = (int)(s - (int64_t)r * H);
-        const int e = p.sorted[r];
-        const bool pair = p.ent[e].w >= 0;
+        const int e = ecached ? ssort[r] : p.sorted[r];
+        const bool pair = ent_at(e).w >= 0;
         const int x = (int)(s & 7);
         const int64_t i = s >> 3;
         int2 *q = p.queue + (int64_t)x * p.qcap + 2 * i;
@@ -257,7 +279,7 @@ struct PieceArgs {
     const int32_t *state_indices;
     float *state_pool;
     const float *M, *U;
-    float *IN;
+    bf16_t *XT;     // [n_piece][H][dv][dk]: incoming state of each later piece, transposed
     const bf16_t *W;
     bf16_t *out;
     int H;
@@ -287,15 +309,20 @@ __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
         }
         for (int i = 0; i < sq.z; ++i) {
             const int64_t kh = (int64_t)(sq.y + i) * H + h;
-            float *inw = p.IN + kh * DK * DV + r * DV + c0;
-            *(f32x4 *)inw = f32x4{x[0], x[1], x[2], x[3]};
-            *(f32x4 *)(inw + 4) = f32x4{x[4], x[5], x[6], x[7]};
+            // the correction's MFMA reads X^T rows (one column of X) as bf16
+            bf16_t *xt = p.XT + kh * DV * DK + (int64_t)c0 * DK + r;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) xt[c * DK] = (bf16_t)x[c];
             __syncthreads();
 #pragma unroll
             for (int c = 0; c < 8; ++c) sx[r][8 * half + c] = x[c];
             __syncthreads();
             const float *Mr = p.M + kh * DK * DK + r * DK;
             const float *Ur = p.U + kh * DK * DV + r * DV + c0;
+            // the whole row of M_k is loaded before the first FMA: one memory latency
+            f32x4 mrow[DK / 4];
+#pragma unroll
+            for (int q = 0; q < DK / 4; ++q) mrow[q] = *(const f32x4 *)(Mr + 4 * q);
             const f32x4 u0 = *(const f32x4 *)Ur, u1 = *(const f32x4 *)(Ur + 4);
             float y[8];
 #pragma unroll
@@ -304,13 +331,12 @@ __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
                 y[c + 4] = u1[c];
             }
             // X_{k+1} = M_k X_k + U_k, fp32, keys in order
-            for (int k0 = 0; k0 < DK; k0 += 4) {
-                const f32x4 m = *(const f32x4 *)(Mr + k0);
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < DK / 4; ++q)
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) y[c] = fmaf(m[q], sx[k0 + q][8 * half + c], y[c]);
-            }
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) y[c] = fmaf(mrow[q][e], sx[4 * q + e][8 * half + c], y[c]);
 #pragma unroll
             for (int c = 0; c < 8; ++c) x[c] = y[c];
         }
@@ -321,13 +347,11 @@ __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
 }
 
 // out_t += W_t X_k for every token of every later piece.  Task = (piece, head, chunk),
-// numbered piece-major so that a workgroup's contiguous share of tasks reuses X_k^T,
-// staged once in LDS as bf16.  Wave w computes columns 32w .. 32w+31 as
-// C^T = X^T W^T (16x16x32 bf16 MFMA), so that each lane adds 4 consecutive columns of one
-// token (one 8-byte read-modify-write).
+// numbered piece-major, so a workgroup's contiguous share of tasks mostly reuses one
+// X_k^T (bf16, written by piece_scan_kernel), held as MFMA fragments in registers.
+// Wave w computes columns 32w .. 32w+31 as C^T = X^T W^T (16x16x32 bf16 MFMA): each lane
+// then adds 4 consecutive columns of one token (one 8-byte read-modify-write).
 __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
-    constexpr int PX = DK + 8;
-    __shared__ __attribute__((aligned(16))) bf16_t sxt[DV * PX];
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
     const int H = p.H;
     const int n_piece = p.hdr->n_piece;
@@ -335,6 +359,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
     const int64_t per = (n_tasks + gridDim.x - 1) / gridDim.x;
     const int64_t lo_t = (int64_t)blockIdx.x * per, hi_t = min(n_tasks, lo_t + per);
     int cur = -1;
+    bf16x8 xa[2][4];
     for (int64_t task = lo_t; task < hi_t; ++task) {
         int lo = 0, hi = n_piece - 1;  // last piece whose task range starts at or before task
         while (lo < hi) {
@@ -348,34 +373,41 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         const int h = (int)(rem / len), c = (int)(rem - (int64_t)h * len);
         const int key = lo * H + h;
         if (key != cur) {
-            __syncthreads();
-            const float *X = p.IN + ((int64_t)lo * H + h) * DK * DV;
-            for (int e = t; e < DK * DV / 4; e += 256) {
-                const int kr = e >> 5, c4 = (e & 31) * 4;
-                const f32x4 v = *(const f32x4 *)(X + kr * DV + c4);
+            const bf16_t *xt = p.XT + (int64_t)key * DV * DK;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) sxt[(c4 + q) * PX + kr] = (bf16_t)v[q];
-            }
-            __syncthreads();
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    xa[ct][kb] = *(const bf16x8 *)(xt + (32 * w + 16 * ct + li) * DK + 32 * kb + 8 * g);
             cur = key;
         }
         const int s0 = p.cu[pc.x], s1 = p.cu[pc.x + 1];
         const int t0 = s0 + 64 * (pc.y + c);
         const int n = min(64, s1 - t0);
-        for (int tt = 0; tt < 4 && 16 * tt < n; ++tt) {
-            const int row = t0 + min(16 * tt + li, n - 1);
-            const bf16_t *wr = p.W + ((int64_t)row * H + h) * DV;
-            f32x4 acc0 = zero4(), acc1 = zero4();
+        // every load of the task first (rows past the end repeat the last row and are
+        // not stored), so the task waits for memory once
+        bf16x8 bw[4][4];
+        bf16x4 ov[4][2];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int64_t rowh = (int64_t)(t0 + min(16 * tt + li, n - 1)) * H + h;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) bw[tt][kb] = *(const bf16x8 *)(p.W + rowh * DV + 32 * kb + 8 * g);
+            ov[tt][0] = *(const bf16x4 *)(p.out + rowh * DV + 32 * w + 4 * g);
+            ov[tt][1] = *(const bf16x4 *)(p.out + rowh * DV + 32 * w + 16 + 4 * g);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f32x4 acc0 = f4(ov[tt][0]), acc1 = f4(ov[tt][1]);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const bf16x8 bw = *(const bf16x8 *)(wr + 32 * kb + 8 * g);
-                acc0 = mfma(*(const bf16x8 *)(sxt + (32 * w + li) * PX + 32 * kb + 8 * g), bw, acc0);
-                acc1 = mfma(*(const bf16x8 *)(sxt + (32 * w + 16 + li) * PX + 32 * kb + 8 * g), bw, acc1);
+                acc0 = mfma(xa[0][kb], bw[tt][kb], acc0);
+                acc1 = mfma(xa[1][kb], bw[tt][kb], acc1);
             }
             if (16 * tt + li < n) {
                 bf16_t *o = p.out + ((int64_t)(t0 + 16 * tt + li) * H + h) * DV + 32 * w + 4 * g;
-                *(bf16x4 *)o = bf4(f4(*(const bf16x4 *)o) + acc0);
-                *(bf16x4 *)(o + 16) = bf4(f4(*(const bf16x4 *)(o + 16)) + acc1);
+                *(bf16x4 *)o = bf4(acc0);
+                *(bf16x4 *)(o + 16) = bf4(acc1);
             }
         }
     }
@@ -410,8 +442,8 @@ PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_cu) {
     o = plan::align256(o + (size_t)y.np_cap * H * dk * dk * sizeof(float));
     y.U = o;
     o = plan::align256(o + st);
-    y.IN = o;
-    o = plan::align256(o + st);
+    y.XT = o;  // X^T of the later pieces, bf16
+    o = plan::align256(o + (size_t)y.np_cap * H * dk * dv * sizeof(bf16_t));
     y.W = o;
     o = plan::align256(o + (size_t)T * H * dv * sizeof(bf16_t));
     y.total = o;
@@ -456,14 +488,17 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     pp.state_pool = a.state_pool;
     pp.M = a.ws_M;
     pp.U = a.ws_U;
-    pp.IN = (float *)(ws + lay.IN);
+    pp.XT = (bf16_t *)(ws + lay.XT);
     pp.W = (const bf16_t *)a.ws_W;
     pp.out = (bf16_t *)a.out;
     pp.H = a.H;
-    hipLaunchKernelGGL(plan::piece_scan_kernel, dim3(n_cu), dim3(256), 0, stream, pp);
+    // grids sized from capacities (the counts are known on the device only): every scan
+    // task of a full plan at once; surplus workgroups find no task and exit
+    const int scan_grid = min(lay.np_cap * a.H * (plan::DV / 16), 4 * n_cu);
+    hipLaunchKernelGGL(plan::piece_scan_kernel, dim3(scan_grid), dim3(256), 0, stream, pp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(plan::fixup_kernel, dim3(2 * n_cu), dim3(256), 0, stream, pp);
+    hipLaunchKernelGGL(plan::fixup_kernel, dim3(8 * n_cu), dim3(256), 0, stream, pp);
     return hipGetLastError();
 }
 
