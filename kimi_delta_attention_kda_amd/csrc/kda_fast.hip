@@ -281,7 +281,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
         } else if (q == 1) {
             praw[2] = *(const f32x4 *)(rg + roff[2]);
             praw[3] = *(const f32x4 *)(rg + roff[3]);
-            if (t < 64) pbl = a.beta_logits[rb + (unsigned)(min(t, t_end - t0 - 1) * H)];
+            pbl = a.beta_logits[rb + (unsigned)(min(l, t_end - t0 - 1) * H)];
         } else if (q == 2) {
 #pragma unroll
             for (int r = 0; r < 3; ++r) pk[r] = *(const bf16x4 *)(kp + roff[r]);
@@ -303,36 +303,28 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 for (int r = 1; r < 4; ++r) pv[r] = *(const bf16x4 *)(vp + roff[r]);
         }
     };
-    if (n_chunks > 0)
-#pragma unroll
-        for (int q = 0; q < 6; ++q) issue(0, q);
-
-    for (int ck = 0; ck < n_chunks; ++ck) {
-        const int t0 = t_begin + ck * 64;
-        const int n = min(64, t_end - t0);
-
-        // ============ P0: gate, running products, score operands, V^T ============
-        bf16x4 kr4[4], qr4[4];
-        float kc[4][4];
+    // ---- software pipeline over chunks: the gate and decay products of chunk c+1 (VALU
+    // work, branch-free) are computed while the outputs and the state update of chunk c
+    // (MFMA and LDS work) run.  They write only arrays that the rest of chunk c no longer
+    // reads (Kr, Qr, Kc, block decays, V^T, beta).
+    bf16x4 kr4[4], qr4[4];
+    float kc[4][4];
+    auto prep0 = [&](int ck) {
+        const int n = min(64, t_end - (t_begin + ck * 64));
         {
             // Rows past the sequence end hold a copy of its last row: only their gate
             // (alpha = 1) and beta (0) are masked; with beta = 0 they add nothing to A, R, U
             // or the state, and their outputs are never stored.
             float al[4][4], kf[4][4], qf[4][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 4; ++r) {
+                const float floor_r = rbase + r < n ? amin : 1.f;  // alpha <= 1: padded rows get 1
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
-                    al[r][cc] = gate_alpha(praw[r][cc], dtb[cc], negA, amin);
+                    al[r][cc] = gate_alpha(praw[r][cc], dtb[cc], negA, floor_r);
                     kf[r][cc] = (float)pk[r][cc];
                     qf[r][cc] = FW ? (float)pq[r][cc] : 0.f;
                 }
-            if (n < 64) {  // last, partial chunk of the sequence (wave-uniform branch)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int cc = 0; cc < 4; ++cc)
-                        if (rbase + r >= n) al[r][cc] = 1.f;
             }
             // products over this quarter block, then over the other quarters (quad lanes)
             f32x4 E, pre, suf;
@@ -376,12 +368,11 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 for (int cc = 0; cc < 4; ++cc) kcb[cc] = (bf16_t)kc[r][cc];
                 *(bf16x4 *)(sKC + i * PK + c0) = kcb;
             }
-            if (rq == 0) {
-                *(f32x4 *)(sE + I * DK + c0) = E;
-                // 1/E <= e^{16 |bound|}: finite under the safe gate
-                *(f32x4 *)(sIE + I * DK + c0) = f32x4{__builtin_amdgcn_rcpf(E[0]), __builtin_amdgcn_rcpf(E[1]),
-                                                     __builtin_amdgcn_rcpf(E[2]), __builtin_amdgcn_rcpf(E[3])};
-            }
+            // the four lanes of a quad hold the same E: unconditional identical stores
+            *(f32x4 *)(sE + I * DK + c0) = E;
+            // 1/E <= e^{16 |bound|}: finite under the safe gate
+            *(f32x4 *)(sIE + I * DK + c0) = f32x4{__builtin_amdgcn_rcpf(E[0]), __builtin_amdgcn_rcpf(E[1]),
+                                                 __builtin_amdgcn_rcpf(E[2]), __builtin_amdgcn_rcpf(E[3])};
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
                 bf16x4 v4;
@@ -389,9 +380,26 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 for (int r = 0; r < 4; ++r) v4[r] = pv[r][cc];
                 *(bf16x4 *)(sVT + (c0 + cc) * PJ + rbase) = v4;
             }
-            if (t < 64) sBeta[t] = (t < n) ? (a.beta_mode == 0 ? 1.f / (1.f + __expf(-pbl)) : pbl) : 0.f;
+            // every wave holds the 64 beta logits of the chunk (identical stores)
+            sBeta[l] = l < n ? (a.beta_mode == 0 ? 1.f / (1.f + __expf(-pbl)) : pbl) : 0.f;
         }
+    };
+    if (n_chunks > 0) {
+#pragma unroll
+        for (int q = 0; q < 6; ++q) issue(0, q);
+        prep0(0);
         __syncthreads();
+        if (n_chunks > 1) {
+            issue(1, 0);
+            issue(1, 1);
+            issue(1, 2);
+        }
+    }
+
+    for (int ck = 0; ck < n_chunks; ++ck) {
+        const int t0 = t_begin + ck * 64;
+        const int n = min(64, t_end - t0);
+        const bool more = ck + 1 < n_chunks;
 
         // ============ P1: cross-block factors, chain operands Kg, Qbar, Khat^T ============
         {
@@ -428,8 +436,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
         // (no barrier: Kg, Qbar, Khat^T and e^{G_last} are first read in the chain step)
 
         // next chunk's loads fly while this chunk is computed
-        const bool more = ck + 1 < n_chunks;
-        if (more) issue(ck + 1, 0);
+        if (more) issue(ck + 1, 3);
 
         // ============ P2: decayed scores; diagonal waves also invert their block ============
         {
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                     if (FW) sP[i * PJ + j] = (f16_t)((j <= i) ? accP[s] : 0.f);
                 }
             }
-            if (more) issue(ck + 1, 1);
+            if (more) issue(ck + 1, 4);
             if (w < 4 && l < 16) {
                 // (I + A_ww)^-1, one column per lane, right-looking substitution: as soon as
                 // x_k is final it is folded into every later row, so the dependent chain is
@@ -500,15 +507,17 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 for (int r = 0; r < 16; ++r) sD[(w * 16 + r) * 24 + col] = (f16_t)x[r];
             }
         }
+        if (more) issue(ck + 1, 5);
         __syncthreads();
 
-        // ============ P3: chain step of value tile w ============
-        if (more) issue(ck + 1, 2);
+        // ============ chain step, first half: Y = Kg S, Z = S^T Qbar^T, R, forward substitution ============
+        f32x4 Z[4];
+        f16x4 Uh[4], Ul[4];
         {
             bf16x8 Sb[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) Sb[kb] = cat(bf4(S[2 * kb]), bf4(S[2 * kb + 1]));
-            f32x4 Y[4], Z[4];
+            f32x4 Y[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 Y[rt] = zero4();
@@ -521,10 +530,8 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                         Z[rt] = mfma(Sb[kb], *(const bf16x8 *)(sQB + (16 * rt + li) * PK + 32 * kb + 8 * g), Z[rt]);
                 }
             }
-            if (more) issue(ck + 1, 3);
             // R = beta (V - Kg S); solve (I + A) U = R block by block
             const int vcol = 16 * w + li;
-            f16x4 Uh[4], Ul[4];
 #pragma unroll
             for (int bI = 0; bI < 4; ++bI) {
                 const f32x4 vv = f4(*(const bf16x4 *)(sVT + vcol * PJ + 16 * bI + 4 * g));
@@ -543,7 +550,12 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 u = mfma16h(dd, wl, u);
                 split_h(u, Uh[bI], Ul[bI]);
             }
-            if (more) issue(ck + 1, 4);
+        }
+        __syncthreads();
+
+        // ============ chain step, second half: outputs and state update of chunk ck,
+        // interleaved with the gate and decay products of chunk ck + 1 ============
+        {
             if (FW) {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
@@ -559,7 +571,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                             bf4(a.scale * Z[rt]);
                 }
             }
-            if (more) issue(ck + 1, 5);
+            // unconditional, so that it shares a basic block with the state update: past the
+            // last chunk every row is padding and nothing it writes is read again
+            prep0(ck + 1);
             // S <- Diag(e^{G_last}) S + Khat^T U
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) {
@@ -571,6 +585,11 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                     S[ct] = mfma32h(kh, cath(Ul[2 * jb], Ul[2 * jb + 1]), S[ct]);
                 }
             }
+        }
+        if (ck + 2 < n_chunks) {
+            issue(ck + 2, 0);
+            issue(ck + 2, 1);
+            issue(ck + 2, 2);
         }
         __syncthreads();
     }

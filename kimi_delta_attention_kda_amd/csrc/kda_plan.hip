@@ -40,12 +40,13 @@ static_assert(NBIN == PT, "one bin per planner thread");
 
 struct PlanArgs {
     const int32_t *cu;
+    const int32_t *state_indices;
     int B, H, n_cu;
     PlanHeader *hdr;
     int2 *queue;
     int4 *ent;
-    int4 *piece;   // (sequence, first chunk, end chunk, prefix of later-piece chunks)
-    int4 *sseq;    // (sequence, first later piece, number of later pieces, 0)
+    int4 *piece;   // (first token, end token, chunks, prefix of later-piece chunks)
+    int4 *sseq;    // (sequence, first later piece, number of later pieces, pool slot)
     int *sorted;
     int np_cap, ent_cap, qcap;
 };
@@ -99,6 +100,50 @@ __device__ int block_excl_scan(int v, int64_t *red, int *tot) {
     }
     *tot = all;
     return base + x - v;
+}
+
+// Three exclusive prefix sums at once (one pair of barriers).
+__device__ void block_excl_scan3(int a, int b, int c, int64_t *red, int *ea, int *eb, int *ec, int *ta,
+                                 int *tb, int *tc) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int x = a, y = b, z = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int x1 = __shfl_up(x, o), y1 = __shfl_up(y, o), z1 = __shfl_up(z, o);
+        if (lane >= o) {
+            x += x1;
+            y += y1;
+            z += z1;
+        }
+    }
+    __syncthreads();
+    // per-wave totals: (x, y) packed in red, z in zred
+    __shared__ int zred[PT / 64];
+    if (lane == 63) {
+        red[wv] = (int64_t)(((uint64_t)(uint32_t)y << 32) | (uint32_t)x);
+        zred[wv] = z;
+    }
+    __syncthreads();
+    int bx = 0, by = 0, bz = 0, ax = 0, ay = 0, az = 0;
+#pragma unroll
+    for (int i = 0; i < PT / 64; ++i) {
+        const uint64_t v = (uint64_t)red[i];
+        const int vx = (int)(uint32_t)v, vy = (int)(uint32_t)(v >> 32), vz = zred[i];
+        if (i < wv) {
+            bx += vx;
+            by += vy;
+            bz += vz;
+        }
+        ax += vx;
+        ay += vy;
+        az += vz;
+    }
+    *ea = bx + x - a;
+    *eb = by + y - b;
+    *ec = bz + z - c;
+    *ta = ax;
+    *tb = ay;
+    *tc = az;
 }
 
 __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
@@ -177,10 +222,8 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
             my_e += n - L;
         }
     }
-    int tot_p, tot_s, tot_e;
-    int kb = block_excl_scan(my_p, red, &tot_p);
-    int jb = block_excl_scan(my_s, red, &tot_s);
-    int eb = block_excl_scan(my_e, red, &tot_e);
+    int tot_p, tot_s, tot_e, kb, jb, eb;
+    block_excl_scan3(my_p, my_s, my_e, red, &kb, &jb, &eb, &tot_p, &tot_s, &tot_e);
     if (tot_p > p.np_cap || B + tot_p > p.ent_cap) {  // cannot happen by the sizing; stay safe
         L = 0;
         tot_p = tot_s = tot_e = 0;
@@ -196,11 +239,12 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
         const int n = chunks(b);
         if (split_of(n)) {
             const int R = n - L, P = (R + L - 1) / L, base = R / P, rem = R % P;
-            p.sseq[jb] = make_int4(b, kb, P, 0);
+            p.sseq[jb] = make_int4(b, kb, P, p.state_indices[b]);
+            const int cb = p.cu[b], ce = p.cu[b + 1];
             int c = L;
             for (int i = 0; i < P; ++i) {
                 const int len = base + (i < rem ? 1 : 0);
-                p.piece[kb + i] = make_int4(b, c, c + len, eb);
+                p.piece[kb + i] = make_int4(cb + 64 * c, min(ce, cb + 64 * (c + len)), len, eb);
                 put_ent(B + kb + i, make_int4(b, c, c + len, kb + i));
                 c += len;
                 eb += len;
@@ -297,7 +341,7 @@ __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
         const int h = jh % H, j = jh / H;
         const int4 sq = p.sseq[j];
         const int c0 = 16 * cb + 8 * half;
-        float *slot = p.state_pool + ((int64_t)p.state_indices[sq.x] * H + h) * DK * DV;
+        float *slot = p.state_pool + ((int64_t)sq.w * H + h) * DK * DV;
         float x[8];
         {
             const f32x4 a0 = *(const f32x4 *)(slot + r * DV + c0), a1 = *(const f32x4 *)(slot + r * DV + c0 + 4);
@@ -347,43 +391,44 @@ __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
 }
 
 // out_t += W_t X_k for every token of every later piece.  Task = (piece, head, chunk),
-// numbered piece-major, so a workgroup's contiguous share of tasks mostly reuses one
-// X_k^T (bf16, written by piece_scan_kernel), held as MFMA fragments in registers.
-// Wave w computes columns 32w .. 32w+31 as C^T = X^T W^T (16x16x32 bf16 MFMA): each lane
-// then adds 4 consecutive columns of one token (one 8-byte read-modify-write).
+// numbered piece-major; a workgroup takes a contiguous share of tasks, decodes them from
+// the piece table staged once in LDS, and mostly reuses one X_k^T (bf16, written by
+// piece_scan_kernel), held as MFMA fragments in registers.  Wave w computes columns
+// 32w .. 32w+31 as C^T = X^T W^T (16x16x32 bf16 MFMA): each lane then adds 4 consecutive
+// columns of one token (one 8-byte read-modify-write).
+constexpr int FIX_NP = 1024;  // pieces staged in LDS (more: read from global memory)
+constexpr int FIX_TASKS = 4;  // tasks per workgroup
+
 __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
+    __shared__ int4 spc[FIX_NP];
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
     const int H = p.H;
     const int n_piece = p.hdr->n_piece;
     const int64_t n_tasks = (int64_t)p.hdr->n_echunk * H;
-    const int64_t per = (n_tasks + gridDim.x - 1) / gridDim.x;
-    const int64_t lo_t = (int64_t)blockIdx.x * per, hi_t = min(n_tasks, lo_t + per);
+    if ((int64_t)blockIdx.x * FIX_TASKS >= n_tasks) return;
+    const bool staged = n_piece <= FIX_NP;
+    if (staged)
+        for (int i = t; i < n_piece; i += 256) spc[i] = p.piece[i];
+    __syncthreads();
+    auto piece_at = [&](int i) { return staged ? spc[i] : p.piece[i]; };
     int cur = -1;
     bf16x8 xa[2][4];
-    for (int64_t task = lo_t; task < hi_t; ++task) {
+    // groups of FIX_TASKS consecutive tasks, strided over the grid
+    for (int64_t grp = blockIdx.x; grp * FIX_TASKS < n_tasks; grp += gridDim.x)
+    for (int64_t task = grp * FIX_TASKS; task < min(n_tasks, (grp + 1) * FIX_TASKS); ++task) {
         int lo = 0, hi = n_piece - 1;  // last piece whose task range starts at or before task
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)H * p.piece[mid].w <= task) lo = mid;
+            if ((int64_t)H * piece_at(mid).w <= task) lo = mid;
             else hi = mid - 1;
         }
-        const int4 pc = p.piece[lo];
-        const int len = pc.z - pc.y;
+        const int4 pc = piece_at(lo);
+        const int len = pc.z;
         const int64_t rem = task - (int64_t)H * pc.w;
         const int h = (int)(rem / len), c = (int)(rem - (int64_t)h * len);
         const int key = lo * H + h;
-        if (key != cur) {
-            const bf16_t *xt = p.XT + (int64_t)key * DV * DK;
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-                    xa[ct][kb] = *(const bf16x8 *)(xt + (32 * w + 16 * ct + li) * DK + 32 * kb + 8 * g);
-            cur = key;
-        }
-        const int s0 = p.cu[pc.x], s1 = p.cu[pc.x + 1];
-        const int t0 = s0 + 64 * (pc.y + c);
-        const int n = min(64, s1 - t0);
+        const int t0 = pc.x + 64 * c;
+        const int n = min(64, pc.y - t0);
         // every load of the task first (rows past the end repeat the last row and are
         // not stored), so the task waits for memory once
         bf16x8 bw[4][4];
@@ -395,6 +440,15 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
             for (int kb = 0; kb < 4; ++kb) bw[tt][kb] = *(const bf16x8 *)(p.W + rowh * DV + 32 * kb + 8 * g);
             ov[tt][0] = *(const bf16x4 *)(p.out + rowh * DV + 32 * w + 4 * g);
             ov[tt][1] = *(const bf16x4 *)(p.out + rowh * DV + 32 * w + 16 + 4 * g);
+        }
+        if (key != cur) {
+            const bf16_t *xt = p.XT + (int64_t)key * DV * DK;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    xa[ct][kb] = *(const bf16x8 *)(xt + (32 * w + 16 * ct + li) * DK + 32 * kb + 8 * g);
+            cur = key;
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
@@ -453,6 +507,7 @@ PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_cu) {
 hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int n_cu, hipStream_t stream) {
     plan::PlanArgs pa;
     pa.cu = a.offsets;
+    pa.state_indices = a.state_indices;
     pa.B = a.n_items;
     pa.H = a.H;
     pa.n_cu = n_cu;
@@ -498,7 +553,7 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     hipLaunchKernelGGL(plan::piece_scan_kernel, dim3(scan_grid), dim3(256), 0, stream, pp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(plan::fixup_kernel, dim3(8 * n_cu), dim3(256), 0, stream, pp);
+    hipLaunchKernelGGL(plan::fixup_kernel, dim3(4 * n_cu), dim3(256), 0, stream, pp);
     return hipGetLastError();
 }
 
