@@ -54,7 +54,7 @@ struct Lds {
     static constexpr int VT = KH + DK * PJ * 2;           // V^T           bf16 [DV][PJ]
     static constexpr int AO = VT + DV * PJ * 2;           // -A off-diag   f16 [64][PJ]
     static constexpr int P = AO + 64 * PJ * 2;            // P (FWD)       f16 [64][PJ]
-    static constexpr int AD = P + (FW ? 64 * PJ * 2 : 0); // A diag blocks f32 [4][16][20]
+    static constexpr int AD = P + (FW ? 64 * PJ * 2 : 0); // A diag blocks^T f32 [4][16][20]
     static constexpr int D = AD + 4 * 16 * 20 * 4;        // (I+A_II)^-1   f16 [4][16][24]
     static constexpr int BETA = D + 4 * 16 * 24 * 2;      // f32 [64]
     static constexpr int E = BETA + 64 * 4;               // block decays  f32 [4][DK]
@@ -118,6 +118,17 @@ __device__ __forceinline__ float gate_alpha(float raw, float dtb_l2e, float negA
 template <int Q>
 __device__ __forceinline__ float quad_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), Q * 0x55, 0xF, 0xF, false));
+}
+
+// Step K of the quad-parallel unit-lower substitution (and the following steps): broadcast
+// acc_K from quad lane K/4, fold x_K = -acc_K into this lane's four rows.
+template <int K>
+__device__ __forceinline__ void inv_step(float (&acc)[4], const float *At, int q) {
+    const f32x4 ak = *(const f32x4 *)(At + K * 20 + 4 * q);
+    const float yk = quad_bcast<(K >> 2)>(acc[K & 3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = fmaf(-ak[j], yk, acc[j]);
+    if constexpr (K < 15) inv_step<K + 1>(acc, At, q);
 }
 
 // Block pairs (I, J <= I) of the 4x4 grid of 16x16 score blocks handled by wave w in the
@@ -476,35 +487,33 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                     accA = mfma(aK, bK, accA);
                     if (FW) accP = mfma(*(const bf16x8 *)(sQR + (16 * bI + li) * PK + cc), bK, accP);
                 }
+                f32x4 at;  // diagonal block, stored transposed: column li, rows 4g .. 4g+3
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const int ri = 4 * g + s, i = 16 * bI + ri, j = 16 * bJ + li;
                     const float av = sBeta[i] * accA[s];
-                    if (bI == bJ)
-                        sAD[(bI * 16 + ri) * 20 + li] = (li < ri) ? av : 0.f;
-                    else
-                        sAO[i * PJ + j] = (f16_t)(-av);
+                    at[s] = (li < ri) ? av : 0.f;
+                    if (bI != bJ) sAO[i * PJ + j] = (f16_t)(-av);
                     if (FW) sP[i * PJ + j] = (f16_t)((j <= i) ? accP[s] : 0.f);
                 }
+                if (bI == bJ) *(f32x4 *)(sAD + (bI * 16 + li) * 20 + 4 * g) = at;
             }
             if (more) issue(ck + 1, 4);
-            if (w < 4 && l < 16) {
-                // (I + A_ww)^-1, one column per lane, right-looking substitution: as soon as
-                // x_k is final it is folded into every later row, so the dependent chain is
-                // one FMA per row instead of a full dot product per row.
-                const int col = l;
-                const float *Ab = sAD + w * 16 * 20;
-                float x[16], acc[16];
+            if (w < 4) {
+                // (I + A_ww)^-1 by right-looking substitution, column c = l/4 of the inverse
+                // on the four lanes of a quad, lane quarter q = l%4 holding rows 4q .. 4q+3.
+                // acc_r = sum_j A_rj x_j - delta_rc, so x_k = -acc_k once rows < k are folded
+                // in; step k broadcasts acc_k across the quad and folds x_k into every row
+                // (rows <= k have A_rk = 0).  A is stored transposed: row k of sAD holds
+                // column k, so a lane reads its four A_rk at once.
+                const int c = l >> 2, q = l & 3;
+                const float *At = sAD + w * 16 * 20;
+                float acc[4];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+                for (int j = 0; j < 4; ++j) acc[j] = (4 * q + j == c) ? -1.f : 0.f;
+                inv_step<0>(acc, At, q);
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    x[k] = (k == col) ? 1.f : ((k < col) ? 0.f : -acc[k]);
-#pragma unroll
-                    for (int r = k + 1; r < 16; ++r) acc[r] = fmaf(Ab[r * 20 + k], x[k], acc[r]);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sD[(w * 16 + r) * 24 + col] = (f16_t)x[r];
+                for (int j = 0; j < 4; ++j) sD[(w * 16 + 4 * q + j) * 24 + c] = (f16_t)(0.f - acc[j]);
             }
         }
         if (more) issue(ck + 1, 5);
