@@ -62,14 +62,16 @@ typedef enum { KDA_STATE_K_FIRST = 0, KDA_STATE_V_FIRST = 1 } kda_state_layout;
 
 /*
  * Shapes and modes of one call (max.nn.state_space.kda_chunk, Parameters).
- * num_heads is both the key-head and value-head count (equal counts only).
+ * num_heads is both the key-head and value-head count (equal counts, as in the
+ * gfx950 contract of kda_chunk).
  * Supported contract (anything else -> KDA_ERR_UNSUPPORTED):
  *   qkv_dtype == out_dtype;
  *   bf16: dk == dv in {64, 128}, gate_mode SAFE with -5.3 <= gate_lower_bound <= 0
  *         (the 16-token factorisation of the decay needs 16*|bound| < 85);
  *   f32:  dk == dv == 64 for kda_chunk_fwd; dk == dv in {64, 128} for
  *         kda_segment_summary; either gate mode;
- *   state_layout K_FIRST.
+ *   kda_decode: dk == dv in {64, 128}, bf16 or f32, either gate mode;
+ *   state_layout K_FIRST ([slot][H][dk][dv]) or V_FIRST ([slot][H][dv][dk]).
  */
 typedef struct {
     int64_t total_tokens;    /* T: rows of q, k, v, raw_gate, beta_logits, out   */
@@ -96,7 +98,8 @@ typedef struct {
  *   a_log       [H]          f32
  *   dt_bias     [H, dk]      f32
  *   cu_seqlens  [B+1]        int32, exclusive prefix offsets, cu[0]=0, cu[B]=T
- *   state_pool  [max_slots, H, dk, dv] f32, K_FIRST; the slot state_indices[b]
+ *   state_pool  [max_slots, H, dk, dv] f32 (K_FIRST; V_FIRST: [max_slots, H, dv, dk]);
+ *               the slot state_indices[b]
  *               holds sequence b's incoming state and receives its final state.
  *               No other byte of the pool is read or written.  A sequence of
  *               length 0 leaves its slot untouched.
@@ -139,6 +142,24 @@ kda_status kda_chunk_fwd_ws(const kda_desc *desc, const void *q, const void *k, 
  * compute unit for piece states.
  */
 kda_status kda_chunk_fwd_workspace_size(const kda_desc *desc, size_t *bytes);
+
+/*
+ * Single-token decode (named beside max.nn.state_space.kda_chunk as the path
+ * for one-token steps): one step of the recurrence per sequence, in the order
+ * of the nx_nofloat_kda.nx source's kda_step (decay, delta-write, read):
+ *   S <- Diag(alpha) S;  S <- S + k (beta (v - S^T k))^T;  o = scale * S^T q,
+ * on the pool slot state_indices[b] of each sequence b, in fp32.
+ *   q, k [B, H, dk], v [B, H, dv] (qkv_dtype); raw_gate [B, H, dk] f32;
+ *   beta_logits [B, H] f32; a_log [H]; dt_bias [H, dk]; state_pool as for
+ *   kda_chunk_fwd (per desc->state_layout); state_indices [B] distinct;
+ *   out [B, H, dv] (out_dtype).  desc->total_tokens must equal desc->batch.
+ * Any gate mode and bound (no chunk factorisation is involved).  Other pool
+ * bytes are untouched.
+ */
+kda_status kda_decode(const kda_desc *desc, const void *q, const void *k, const void *v,
+                      const float *raw_gate, const float *beta_logits, const float *a_log,
+                      const float *dt_bias, float *state_pool, const int32_t *state_indices, void *out,
+                      void *stream);
 
 /*
  * Affine summaries of token segments (KDA Context Parallelism, "Theory": each

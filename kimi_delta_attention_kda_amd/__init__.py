@@ -53,12 +53,13 @@ def lib():
         L.kda_chunk_fwd.argtypes = [dp] + [vp] * 12
         L.kda_chunk_fwd_ws.argtypes = [dp] + [vp] * 12 + [C.c_size_t, vp]
         L.kda_chunk_fwd_workspace_size.argtypes = [dp, C.POINTER(C.c_size_t)]
+        L.kda_decode.argtypes = [dp] + [vp] * 11
         L.kda_segment_summary.argtypes = [dp] + [vp] * 7 + [i32, vp, vp, vp]
         L.kda_affine_exclusive_scan.argtypes = [i32, i32, i32, i32] + [vp] * 7
         L.kda_validate_varlen.argtypes = [vp, i32, i64, vp, i32]
         L.kda_status_string.argtypes = [C.c_int]
         L.kda_status_string.restype = C.c_char_p
-        for f in ("kda_chunk_fwd", "kda_chunk_fwd_ws", "kda_chunk_fwd_workspace_size",
+        for f in ("kda_chunk_fwd", "kda_chunk_fwd_ws", "kda_chunk_fwd_workspace_size", "kda_decode",
                   "kda_segment_summary", "kda_affine_exclusive_scan", "kda_validate_varlen"):
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -130,9 +131,10 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
         _need(t_, n_, torch.float32, dev)
     _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
     _need(state_indices, "state_indices", torch.int32, dev)
+    slot_shape = (H, dk, dv) if state_layout == "K_FIRST" else (H, dv, dk)
     if k.shape != (T, H, dk) or v.shape[:2] != (T, H) or raw_gate.shape != (T, H, dk) \
             or beta_logits.shape != (T, H) or a_log.shape != (H,) or dt_bias.shape != (H, dk) \
-            or state_pool.dim() != 4 or state_pool.shape[1:] != (H, dk, dv) \
+            or state_pool.dim() != 4 or state_pool.shape[1:] != slot_shape \
             or state_indices.shape != (B,):
         raise ValueError("ranks and extents of the inputs disagree")
     odt = output_dtype or q.dtype
@@ -155,6 +157,42 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
             ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
             nbytes = need.value
     _check(lib().kda_chunk_fwd_ws(*args, _ptr(ws), nbytes, _stream()))
+    return out
+
+
+def decode(q, k, v, raw_gate, beta_logits, a_log, dt_bias, state_pool, state_indices, *,
+           output_dtype=None, gate_mode="safe", lower_bound=-5.0, beta_mode="logits",
+           state_layout="K_FIRST", scale=None, out=None):
+    """One recurrent step per sequence on its pool slot (single-token decode).
+
+    q, k [B,H,dk]; v [B,H,dv]; raw_gate [B,H,dk] f32; beta_logits [B,H] f32; a_log [H];
+    dt_bias [H,dk]; state_pool [slots,H,dk,dv] (V_FIRST: [slots,H,dv,dk]) f32, mutated at
+    state_indices [B] int32.  Returns out [B,H,dv] in output_dtype (default: q's dtype).
+    """
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for t_, n_ in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t_, n_, q.dtype, dev)
+    for t_, n_ in ((raw_gate, "raw_gate"), (beta_logits, "beta_logits"), (a_log, "a_log"),
+                   (dt_bias, "dt_bias"), (state_pool, "state_pool")):
+        _need(t_, n_, torch.float32, dev)
+    _need(state_indices, "state_indices", torch.int32, dev)
+    slot_shape = (H, dk, dv) if state_layout == "K_FIRST" else (H, dv, dk)
+    if k.shape != (B, H, dk) or v.shape[:2] != (B, H) or raw_gate.shape != (B, H, dk) \
+            or beta_logits.shape != (B, H) or a_log.shape != (H,) or dt_bias.shape != (H, dk) \
+            or state_pool.dim() != 4 or state_pool.shape[1:] != slot_shape or state_indices.shape != (B,):
+        raise ValueError("ranks and extents of the inputs disagree")
+    odt = output_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=odt, device=dev)
+    else:
+        _need(out, "out", odt, dev)
+    d = make_desc(B, B, H, dk, dv, state_pool.shape[0], q.dtype, odt, gate_mode, lower_bound,
+                  beta_mode, state_layout, scale)
+    _check(lib().kda_decode(C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(beta_logits),
+                            _ptr(a_log), _ptr(dt_bias), _ptr(state_pool), _ptr(state_indices), _ptr(out),
+                            _stream()))
     return out
 
 

@@ -25,7 +25,6 @@ kda_status check_desc(const kda_desc *d, bool summary) {
     if (d->gate_mode == KDA_GATE_SAFE && !(d->gate_lower_bound <= 0.f)) return KDA_ERR_ARG;
     if (!summary && !(d->scale == d->scale)) return KDA_ERR_ARG;  // NaN scale
     // ---- supported contract
-    if (d->state_layout != KDA_STATE_K_FIRST) return KDA_ERR_UNSUPPORTED;
     if (d->dk != d->dv) return KDA_ERR_UNSUPPORTED;
     if (!summary && d->qkv_dtype != d->out_dtype) return KDA_ERR_UNSUPPORTED;
     if (d->qkv_dtype == KDA_BF16) {
@@ -50,6 +49,7 @@ kda::ChainArgs base_args(const kda_desc *d) {
     a.lb = d->gate_lower_bound;
     a.beta_mode = d->beta_mode;
     a.scale = d->scale;
+    a.v_first = d->state_layout == KDA_STATE_V_FIRST;
     return a;
 }
 
@@ -194,7 +194,7 @@ const char *kda_status_string(kda_status s) {
         case KDA_ERR_DTYPE: return "unknown dtype code";
         case KDA_ERR_UNSUPPORTED:
             return "arguments outside the supported contract (equal heads and dims, dk in {64,128}, "
-                   "K_FIRST, bf16 needs the safe gate with bound >= -5.3, f32 forward needs dk 64)";
+                   "bf16 prefill needs the safe gate with bound >= -5.3, f32 prefill needs dk 64)";
         case KDA_ERR_ARG: return "bad mode value or scalar";
         case KDA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case KDA_ERR_DATA: return "cu_seqlens or state_indices violate their preconditions";
@@ -248,6 +248,48 @@ kda_status kda_chunk_fwd_workspace_size(const kda_desc *desc, size_t *bytes) {
     kda::PlanLayout lay;
     int n_cu = 0;
     return workspace_bytes_for(desc, bytes, &lay, &n_cu);
+}
+
+kda_status kda_decode(const kda_desc *desc, const void *q, const void *k, const void *v,
+                      const float *raw_gate, const float *beta_logits, const float *a_log,
+                      const float *dt_bias, float *state_pool, const int32_t *state_indices, void *out,
+                      void *stream) {
+    const kda_desc *d = desc;
+    if (!d) return KDA_ERR_NULL;
+    if (d->batch < 0 || d->num_heads <= 0 || d->dk <= 0 || d->dv <= 0 || d->max_slots <= 0) return KDA_ERR_SHAPE;
+    if (d->total_tokens != d->batch) return KDA_ERR_SHAPE;  // one token per sequence
+    if (!valid_dtype(d->qkv_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_DTYPE;
+    if (d->gate_mode != KDA_GATE_ORIGINAL && d->gate_mode != KDA_GATE_SAFE) return KDA_ERR_ARG;
+    if (d->beta_mode != KDA_BETA_LOGITS && d->beta_mode != KDA_BETA_PROBABILITY) return KDA_ERR_ARG;
+    if (d->state_layout != KDA_STATE_K_FIRST && d->state_layout != KDA_STATE_V_FIRST) return KDA_ERR_ARG;
+    if (d->gate_mode == KDA_GATE_SAFE && !(d->gate_lower_bound <= 0.f)) return KDA_ERR_ARG;
+    if (!(d->scale == d->scale)) return KDA_ERR_ARG;
+    // one step needs no chunk factorisation: any gate form, bf16 or f32
+    if (d->dk != d->dv || !(d->dk == 64 || d->dk == 128) || d->qkv_dtype != d->out_dtype) return KDA_ERR_UNSUPPORTED;
+    if (!a_log || !dt_bias || !state_pool || (desc->batch > 0 && !state_indices)) return KDA_ERR_NULL;
+    if (desc->batch > 0 && (!q || !k || !v || !raw_gate || !beta_logits || !out)) return KDA_ERR_NULL;
+    if (desc->batch == 0) return KDA_OK;
+    kda::DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.raw_gate = raw_gate;
+    a.beta_logits = beta_logits;
+    a.a_log = a_log;
+    a.dt_bias = dt_bias;
+    a.state_pool = state_pool;
+    a.state_indices = state_indices;
+    a.out = out;
+    a.B = desc->batch;
+    a.H = desc->num_heads;
+    a.gate_mode = desc->gate_mode;
+    a.lb = desc->gate_lower_bound;
+    a.beta_mode = desc->beta_mode;
+    a.scale = desc->scale;
+    a.v_first = desc->state_layout == KDA_STATE_V_FIRST;
+    const hipError_t e = kda::launch_decode(a, desc->dk, desc->qkv_dtype == KDA_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *v,

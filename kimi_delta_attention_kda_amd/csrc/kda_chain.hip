@@ -227,7 +227,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 const int c = 16 * ct + 4 * g + s;
                 float val;
                 if (FW)
-                    val = a.state_pool[(((int64_t)slot * H + h) * DK + c) * DV + col];
+                    val = a.state_pool[a.v_first ? (((int64_t)slot * H + h) * DV + col) * DK + c
+                                                  : (((int64_t)slot * H + h) * DK + c) * DV + col];
                 else
                     val = (isM && c == col) ? 1.f : 0.f;
                 S[m][ct][s] = val;
@@ -775,7 +776,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
             for (int s = 0; s < 4; ++s) {
                 const int c = 16 * ct + 4 * g + s;
                 if (FW)
-                    a.state_pool[(((int64_t)slot * H + h) * DK + c) * DV + col] = S[m][ct][s];
+                    a.state_pool[a.v_first ? (((int64_t)slot * H + h) * DV + col) * DK + c
+                                         : (((int64_t)slot * H + h) * DK + c) * DV + col] = S[m][ct][s];
                 else if (isM)
                     a.M[(((int64_t)item * H + h) * DK + c) * DK + col] = S[m][ct][s];
                 else

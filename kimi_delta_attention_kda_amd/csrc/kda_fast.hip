@@ -186,6 +186,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     for (int pass = 0;; ++pass) {
         int t_begin, t_end, h;
         int init;      // 0: load the state from fin, 1: identity, 2: zero
+        bool vf = false;  // fin is a pool slot stored [DV][DK]
         bool has_v;
         float *fin;    // [DK][DV] state of this unit: initial (init 0) and final
         bf16_t *obase = (bf16_t *)a.out;
@@ -202,6 +203,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             if (FW) {
                 fin = a.state_pool + ((int64_t)a.state_indices[item] * H + h) * DK * DV;
                 init = 0;
+                vf = a.v_first;
                 has_v = true;
             } else {  // slice 0: transition columns M, slice 1: contribution columns U
                 const bool isM = slice == 0;
@@ -230,6 +232,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             if (role == ROLE_WHOLE) {
                 fin = a.state_pool + ((int64_t)a.state_indices[seq] * H + h) * DK * DV;
                 init = 0;
+                vf = a.v_first;
                 has_v = true;
             } else if (role == ROLE_M) {
                 fin = a.ws_M + ((int64_t)piece * H + h) * DK * DV;
@@ -249,16 +252,18 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
         const f32x4 dtb = *(const f32x4 *)(a.dt_bias + h * DK + c0) * 1.44269504088896341f;
 
     // ---- state tile of wave w: rows 16ct+4g+s, column 16w + li
-    // Lane (g, li) holds key rows key_row(ct, 4g + s) = 8g + (32(ct/2) + 4(ct%2) + s): one
-    // lane pointer per unit plus compile-time row offsets.
+    // Lane (g, li) holds key rows key_row(ct, 4g + s) = 8g + (32(ct/2) + 4(ct%2) + s) of
+    // column 16w + li: one lane pointer per unit plus row offsets times the row stride
+    // (DV for [DK][DV] storage, 1 for a V_FIRST slot).
     f32x4 S[8];
-    const float *sp = fin + 8 * g * DV + 16 * w + li;
+    const float *sp = vf ? fin + (16 * w + li) * DK + 8 * g : fin + 8 * g * DV + 16 * w + li;
+    const int rstride = vf ? 1 : DV;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int rr = 32 * (ct >> 1) + 4 * (ct & 1) + s;
-            S[ct][s] = init == 0 ? sp[rr * DV] : ((init == 1 && 8 * g + rr == 16 * w + li) ? 1.f : 0.f);
+            S[ct][s] = init == 0 ? sp[rr * rstride] : ((init == 1 && 8 * g + rr == 16 * w + li) ? 1.f : 0.f);
         }
 
     // ---- prefetch registers: 4 rows x 4 channels of raw/k/q/v, one beta logit
@@ -605,11 +610,11 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
 
     // ---- final state of this tile
     {
-        float *fp = fin + 8 * g * DV + 16 * w + li;
+        float *fp = vf ? fin + (16 * w + li) * DK + 8 * g : fin + 8 * g * DV + 16 * w + li;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) fp[(32 * (ct >> 1) + 4 * (ct & 1) + s) * DV] = S[ct][s];
+            for (int s = 0; s < 4; ++s) fp[(32 * (ct >> 1) + 4 * (ct & 1) + s) * rstride] = S[ct][s];
     }
     }  // units
 }

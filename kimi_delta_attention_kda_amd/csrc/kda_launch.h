@@ -57,6 +57,7 @@ struct ChainArgs {
     float lb;
     int beta_mode;
     float scale;
+    int v_first;             // pool slots stored [dv][dk] (V_FIRST) instead of [dk][dv]
     // load-balanced forward pass: when plan is set, workgroups take units from the
     // per-XCD queues instead of one (item, head) each
     const PlanHeader *plan;
@@ -81,6 +82,25 @@ hipError_t launch_fast_planned(const ChainArgs &a, int n_cu, hipStream_t stream)
 // Planner, piece-state scan and output correction of the load-balanced forward pass
 // (bf16, dk = dv = 128).  ws is the workspace laid out by plan_layout.
 hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int n_cu, hipStream_t stream);
+
+struct DecodeArgs {
+    const void *q, *k, *v;        // [B, H, dk] / [B, H, dv], one token per sequence
+    const float *raw_gate;        // [B, H, dk]
+    const float *beta_logits;     // [B, H]
+    const float *a_log;           // [H]
+    const float *dt_bias;         // [H, dk]
+    float *state_pool;            // [slots, H, dk, dv] (or [.., dv, dk] when v_first)
+    const int32_t *state_indices; // [B]
+    void *out;                    // [B, H, dv]
+    int B, H;
+    int gate_mode;
+    float lb;
+    int beta_mode;
+    float scale;
+    int v_first;
+};
+// dk = dv in {64, 128}; bf16 or f32 q/k/v/out.
+hipError_t launch_decode(const DecodeArgs &a, int dk, bool bf16, hipStream_t stream);
 
 hipError_t launch_affine_scan(int n_seg, int H, int dk, int dv, const float *M, const float *U,
                               const float *S_init, float *incoming, float *outgoing, float *final_state,

@@ -327,6 +327,7 @@ struct PieceArgs {
     const bf16_t *W;
     bf16_t *out;
     int H;
+    int v_first;    // pool slots stored [dv][dk]
 };
 
 // Incoming states of the later pieces, in order, and the final state into the slot.
@@ -343,7 +344,10 @@ __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
         const int c0 = 16 * cb + 8 * half;
         float *slot = p.state_pool + ((int64_t)sq.w * H + h) * DK * DV;
         float x[8];
-        {
+        if (p.v_first) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = slot[(c0 + c) * DK + r];
+        } else {
             const f32x4 a0 = *(const f32x4 *)(slot + r * DV + c0), a1 = *(const f32x4 *)(slot + r * DV + c0 + 4);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -384,8 +388,13 @@ __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) x[c] = y[c];
         }
-        *(f32x4 *)(slot + r * DV + c0) = f32x4{x[0], x[1], x[2], x[3]};
-        *(f32x4 *)(slot + r * DV + c0 + 4) = f32x4{x[4], x[5], x[6], x[7]};
+        if (p.v_first) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) slot[(c0 + c) * DK + r] = x[c];
+        } else {
+            *(f32x4 *)(slot + r * DV + c0) = f32x4{x[0], x[1], x[2], x[3]};
+            *(f32x4 *)(slot + r * DV + c0 + 4) = f32x4{x[4], x[5], x[6], x[7]};
+        }
         __syncthreads();
     }
 }
@@ -547,6 +556,7 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     pp.W = (const bf16_t *)a.ws_W;
     pp.out = (bf16_t *)a.out;
     pp.H = a.H;
+    pp.v_first = a.v_first;
     // grids sized from capacities (the counts are known on the device only): every scan
     // task of a full plan at once; surplus workgroups find no task and exit
     const int scan_grid = min(lay.np_cap * a.H * (plan::DV / 16), 4 * n_cu);

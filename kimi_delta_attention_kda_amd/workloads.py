@@ -145,6 +145,8 @@ def make_inputs(w: Workload, device="cpu") -> dict:
     v = normal(T, H, dv).to(dt)
     raw_gate = normal(T, H, dk) + w.raw_mean
     beta_logits = normal(T, H, std=w.beta_sigma) + w.beta_mean
+    if w.beta_mode == 1:  # beta given directly as a probability: uniform in (0, 1)
+        beta_logits = torch.rand(T, H, generator=g, device=device, dtype=torch.float32)
     a_log = torch.rand(H, generator=g, device=device, dtype=torch.float32) * w.a_log_hi
     dt_bias = normal(H, dk, std=0.1)
 

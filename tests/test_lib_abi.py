@@ -83,9 +83,12 @@ def test_chunk_fwd_error_paths(L):
     assert _fwd(L, _desc(dk=96, dv=96)) == EUNSUP
     assert _fwd(L, _desc(out_dtype=torch.float32)) == EUNSUP
     assert _fwd(L, _desc(qkv_dtype=torch.float32, out_dtype=torch.float32)) == EUNSUP  # f32 fwd: dk 64
+    d = _desc(dk=96, dv=96)
+    d.state_layout = 1                                              # V_FIRST is in the contract;
+    assert _fwd(L, d) == EUNSUP                                     # dk 96 is not
     d = _desc()
-    d.state_layout = 1
-    assert _fwd(L, d) == EUNSUP                                     # V_FIRST
+    d.state_layout = 2
+    assert _fwd(L, d) == EARG
     d = _desc()
     d.gate_mode = 7
     assert _fwd(L, d) == EARG
@@ -127,6 +130,25 @@ def test_workspace_variant_error_paths(L):
     assert st in (OK, 6)
     if st == OK:
         assert n.value >= 128 * 4 * 128 * 2
+
+
+def _dec(L, d, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, raw=FAKE, beta=FAKE, a_log=FAKE, dtb=FAKE, pool=FAKE, idx=FAKE, out=FAKE)
+    p.update(ptrs)
+    return L.kda_decode(C.byref(d) if d is not None else None, p["q"], p["k"], p["v"], p["raw"], p["beta"],
+                        p["a_log"], p["dtb"], p["pool"], p["idx"], p["out"], None)
+
+
+def test_decode_error_paths(L):
+    assert _dec(L, None) == ENULL
+    assert _dec(L, _desc(T=8, B=4)) == ESHAPE                     # one token per sequence
+    assert _dec(L, _desc(T=4, B=4), q=None) == ENULL
+    assert _dec(L, _desc(T=4, B=4), pool=None) == ENULL
+    assert _dec(L, _desc(T=4, B=4, dk=96, dv=96)) == EUNSUP
+    assert _dec(L, _desc(T=4, B=4, dk=128, dv=64)) == EUNSUP
+    assert _dec(L, _desc(T=4, B=4, qkv_dtype=torch.float16)) == EDTYPE
+    assert _dec(L, _desc(T=4, B=4, lower_bound=0.5)) == EARG
+    assert _dec(L, _desc(T=0, B=0)) == OK                         # nothing to do, nothing launched
 
 
 def test_summary_and_scan_error_paths(L):
