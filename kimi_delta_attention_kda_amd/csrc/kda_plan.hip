@@ -337,8 +337,11 @@ __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
     const int t = threadIdx.x, H = p.H;
     const int r = t >> 1, half = t & 1;
     const int n_tasks = p.hdr->n_split * H * (DV / 16);
-    for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
-        const int cb = task & 7, jh = task >> 3;
+    // The 8 column blocks of one (sequence, head) read the same M_k: keep them on one XCD
+    // (workgroups are dealt to the XCDs round-robin), so M_k comes from HBM once.
+    for (int lin = blockIdx.x; lin < ((n_tasks + 63) & ~63); lin += gridDim.x) {
+        const int cb = (lin >> 3) & 7, jh = ((lin >> 6) << 3) | (lin & 7);
+        if (jh >= p.hdr->n_split * H) continue;
         const int h = jh % H, j = jh / H;
         const int4 sq = p.sseq[j];
         const int c0 = 16 * cb + 8 * half;
@@ -559,7 +562,7 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     pp.v_first = a.v_first;
     // grids sized from capacities (the counts are known on the device only): every scan
     // task of a full plan at once; surplus workgroups find no task and exit
-    const int scan_grid = min(lay.np_cap * a.H * (plan::DV / 16), 4 * n_cu);
+    const int scan_grid = min((lay.np_cap * a.H * (plan::DV / 16) + 63) & ~63, 4 * n_cu);
     hipLaunchKernelGGL(plan::piece_scan_kernel, dim3(scan_grid), dim3(256), 0, stream, pp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
