@@ -8,8 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_chain.hip", "kda_decode.hip", "kda_fast.hip", "kda_plan.hip", "kda_scan.hip"]
-HEADERS = ["kda_common.h", "kda_launch.h"]
+SOURCES = ["kda_api.hip", "kda_chain.hip", "kda_decode.hip", "kda_fast.hip", "kda_fast32.hip", "kda_plan.hip", "kda_scan.hip"]
+HEADERS = ["kda_common.h", "kda_fast_common.h", "kda_launch.h"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

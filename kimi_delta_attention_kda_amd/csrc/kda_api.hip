@@ -109,13 +109,16 @@ hipMemPool_t device_pool(int dev) {
 
 bool planned_applies(const kda_desc *d) { return use_fast(d) && d->batch > 0 && d->total_tokens > 0; }
 
+// chunk kernel of the bf16 dk = dv = 128 forward pass
+const kda::FwdKernel &fwd_kernel() { return kda::FWD64; }
+
 kda_status workspace_bytes_for(const kda_desc *d, size_t *bytes, kda::PlanLayout *lay, int *n_cu) {
     *bytes = 0;
     if (!planned_applies(d)) return KDA_OK;
     int dev = 0;
     const int cus = current_device_cus(&dev);
     if (cus <= 0) return KDA_ERR_HIP;
-    *lay = kda::plan_layout(d->total_tokens, d->batch, d->num_heads, d->dk, d->dv, cus);
+    *lay = kda::plan_layout(d->total_tokens, d->batch, d->num_heads, d->dk, d->dv, fwd_kernel().per_cu * cus);
     *bytes = lay->total;
     *n_cu = cus;
     return KDA_OK;
@@ -170,7 +173,9 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
             st = workspace_bytes_for(desc, &need, &lay, &n_cu);
             if (st != KDA_OK) return st;
             if (workspace_bytes < need) return KDA_ERR_SHAPE;
-            e = kda::launch_planned_fwd(a, (char *)workspace, lay, n_cu, (hipStream_t)stream);
+            e = kda::launch_planned_fwd(a, (char *)workspace, lay, n_cu, fwd_kernel(), (hipStream_t)stream);
+        } else if (fwd_kernel().chunk == 32) {
+            e = kda::launch_fast32(a, (hipStream_t)stream);
         } else {
             e = kda::launch_fast(a, kda::MODE_FWD, (hipStream_t)stream);
         }

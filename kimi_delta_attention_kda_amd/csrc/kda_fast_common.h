@@ -1,0 +1,83 @@
+// kda_fast_common.h -- device helpers shared by the chunk kernels for dk = dv = 128
+// (kda_fast.hip: 64-token chunks, 8 waves; kda_fast32.hip: 32-token chunks, 4 waves).
+#pragma once
+
+#include "kda_common.h"
+
+namespace kda {
+namespace fk {
+
+typedef _Float16 f16_t;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma16h(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma32h(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 cath(f16x4 a, f16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Key channel held in row rho of the state's 16-row tile ct.  Tiles 2kb and 2kb+1 hold
+// channels 32kb + 8(rho/4) + {0..3} and {4..7}: the k slots s of lane group g in the
+// products with the state are then channels 32kb + 8g + s.
+__device__ __forceinline__ int key_row(int ct, int rho) {
+    return 32 * (ct >> 1) + 8 * (rho >> 2) + 4 * (ct & 1) + (rho & 3);
+}
+// Inverse: the tile row (16 ct + rho) of key channel c.  Khat^T is stored in this row
+// order so that the state update reads 16 consecutive rows per fragment.
+__device__ __forceinline__ int tile_row(int c) {
+    return 16 * (2 * (c >> 5) + ((c >> 2) & 1)) + 4 * ((c >> 3) & 3) + (c & 3);
+}
+
+// A-operand fragment whose k slots follow the accumulator row order of two 16-row
+// tiles: slot s<4 -> column k0+4g+s, slot s>=4 -> column k0+16+4g+(s-4).
+__device__ __forceinline__ bf16x8 fragA_perm(const bf16_t *base, int pitch, int row, int k0, int g) {
+    const bf16_t *p = base + row * pitch + k0 + 4 * g;
+    return cat(*(const bf16x4 *)p, *(const bf16x4 *)(p + 16));
+}
+__device__ __forceinline__ f16x8 fragA_perm_h(const f16_t *base, int pitch, int row, int k0, int g) {
+    const f16_t *p = base + row * pitch + k0 + 4 * g;
+    return cath(*(const f16x4 *)p, *(const f16x4 *)(p + 16));
+}
+
+__device__ __forceinline__ void split_h(f32x4 x, f16x4 &hi, f16x4 &lo) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        hi[s] = (f16_t)x[s];
+        lo[s] = (f16_t)fmaf((float)hi[s], -1.f, x[s]);  // x - hi, exact
+    }
+}
+
+// alpha = exp(-A softplus(x)) = (1 + e^x)^(-A), computed as 2^(-A log2(1 + 2^(x log2 e)));
+// the safe gate's floor on log alpha is a floor exp(bound) on alpha.  Branch-free: the
+// three transcendentals are the hardware base-2 exp/log.
+__device__ __forceinline__ float gate_alpha(float raw, float dtb_l2e, float negA, float amin) {
+    // dtb_l2e = dt_bias * log2(e): one FMA forms (raw + dt_bias) log2(e)
+    const float t = __builtin_amdgcn_exp2f(fmaf(raw, 1.44269504088896341f, dtb_l2e));
+    const float a = __builtin_amdgcn_exp2f(negA * __builtin_amdgcn_logf(1.f + t));
+    return fmaxf(a, amin);
+}
+
+// value held by lane q of this lane's quad (DPP quad permutation [q, q, q, q])
+template <int Q>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), Q * 0x55, 0xF, 0xF, false));
+}
+
+// Step K of the quad-parallel unit-lower substitution (and the following steps): broadcast
+// acc_K from quad lane K/4, fold x_K = -acc_K into this lane's four rows.
+template <int K>
+__device__ __forceinline__ void inv_step(float (&acc)[4], const float *At, int q) {
+    const f32x4 ak = *(const f32x4 *)(At + K * 20 + 4 * q);
+    const float yk = quad_bcast<(K >> 2)>(acc[K & 3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = fmaf(-ak[j], yk, acc[j]);
+    if constexpr (K < 15) inv_step<K + 1>(acc, At, q);
+}
+
+}  // namespace fk
+}  // namespace kda

@@ -41,7 +41,8 @@ static_assert(NBIN == PT, "one bin per planner thread");
 struct PlanArgs {
     const int32_t *cu;
     const int32_t *state_indices;
-    int B, H, n_cu;
+    int B, H, n_cu;  // n_cu: workgroups of the chunk kernel that run at once
+    int cs;          // tokens per chunk
     PlanHeader *hdr;
     int2 *queue;
     int4 *ent;
@@ -51,9 +52,9 @@ struct PlanArgs {
     int np_cap, ent_cap, qcap;
 };
 
-__device__ __forceinline__ int chunks_of(const int32_t *cu, int b) {
+__device__ __forceinline__ int chunks_of(const int32_t *cu, int b, int cs) {
     const int len = cu[b + 1] - cu[b];
-    return len > 0 ? (len + 63) / 64 : 0;
+    return len > 0 ? (len + cs - 1) / cs : 0;
 }
 
 // Sum / max over the workgroup; every thread gets the result.
@@ -156,9 +157,9 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
     const int B = p.B, H = p.H;
     const bool cached = B <= NCACHE;
     if (cached)
-        for (int b = t; b < B; b += PT) sn[b] = chunks_of(p.cu, b);
+        for (int b = t; b < B; b += PT) sn[b] = chunks_of(p.cu, b, p.cs);
     __syncthreads();
-    auto chunks = [&](int b) { return cached ? sn[b] : chunks_of(p.cu, b); };
+    auto chunks = [&](int b) { return cached ? sn[b] : chunks_of(p.cu, b, p.cs); };
 
     // ---- chunk totals
     int64_t s_loc = 0;
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
             int c = L;
             for (int i = 0; i < P; ++i) {
                 const int len = base + (i < rem ? 1 : 0);
-                p.piece[kb + i] = make_int4(cb + 64 * c, min(ce, cb + 64 * (c + len)), len, eb);
+                p.piece[kb + i] = make_int4(cb + p.cs * c, min(ce, cb + p.cs * (c + len)), len, eb);
                 put_ent(B + kb + i, make_int4(b, c, c + len, kb + i));
                 c += len;
                 eb += len;
@@ -328,6 +329,7 @@ struct PieceArgs {
     bf16_t *out;
     int H;
     int v_first;    // pool slots stored [dv][dk]
+    int cs;         // tokens per chunk (a correction task covers one chunk)
 };
 
 // Incoming states of the later pieces, in order, and the final state into the slot.
@@ -439,14 +441,17 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         const int64_t rem = task - (int64_t)H * pc.w;
         const int h = (int)(rem / len), c = (int)(rem - (int64_t)h * len);
         const int key = lo * H + h;
-        const int t0 = pc.x + 64 * c;
-        const int n = min(64, pc.y - t0);
+        const int t0 = pc.x + p.cs * c;
+        const int n = min(p.cs, pc.y - t0);
         // every load of the task first (rows past the end repeat the last row and are
         // not stored), so the task waits for memory once
+        // (at most four 16-token tiles: chunks of 32 or 64 tokens)
         bf16x8 bw[4][4];
         bf16x4 ov[4][2];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
+            if (16 * tt >= p.cs) break;
+            // rows past the chunk's end repeat its last row and are not stored
             const int64_t rowh = (int64_t)(t0 + min(16 * tt + li, n - 1)) * H + h;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) bw[tt][kb] = *(const bf16x8 *)(p.W + rowh * DV + 32 * kb + 8 * g);
@@ -464,6 +469,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
+            if (16 * tt >= p.cs) break;
             f32x4 acc0 = f4(ov[tt][0]), acc1 = f4(ov[tt][1]);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -483,11 +489,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace plan
 
-PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_cu) {
+PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_slots) {
     PlanLayout y;
-    // later pieces per head <= total chunks / L <= n_cu / H (L is at least the average
+    // later pieces per head <= total chunks / L <= n_slots / H (L is at least the average
     // load); twice that plus slack
-    y.np_cap = 2 * ((n_cu + H - 1) / H) + 2;
+    y.np_cap = 2 * ((n_slots + H - 1) / H) + 2;
     y.ent_cap = B + y.np_cap;
     y.qcap = (int)(2 * (((int64_t)y.ent_cap * H + 7) / 8) + 2);
     size_t o = 0;
@@ -516,13 +522,15 @@ PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_cu) {
     return y;
 }
 
-hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int n_cu, hipStream_t stream) {
+hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int n_cu, const FwdKernel &fk,
+                              hipStream_t stream) {
     plan::PlanArgs pa;
     pa.cu = a.offsets;
     pa.state_indices = a.state_indices;
     pa.B = a.n_items;
     pa.H = a.H;
-    pa.n_cu = n_cu;
+    pa.n_cu = fk.per_cu * n_cu;
+    pa.cs = fk.chunk;
     pa.hdr = (PlanHeader *)(ws + lay.hdr);
     pa.queue = (int2 *)(ws + lay.queue);
     pa.ent = (int4 *)(ws + lay.ent);
@@ -543,7 +551,7 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     a.ws_M = (float *)(ws + lay.M);
     a.ws_U = (float *)(ws + lay.U);
     a.ws_W = ws + lay.W;
-    e = launch_fast_planned(a, n_cu, stream);
+    e = fk.chunk == 32 ? launch_fast32_planned(a, fk.per_cu * n_cu, stream) : launch_fast_planned(a, n_cu, stream);
     if (e != hipSuccess) return e;
 
     plan::PieceArgs pp;
@@ -560,6 +568,7 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     pp.out = (bf16_t *)a.out;
     pp.H = a.H;
     pp.v_first = a.v_first;
+    pp.cs = fk.chunk;
     // grids sized from capacities (the counts are known on the device only): every scan
     // task of a full plan at once; surplus workgroups find no task and exit
     const int scan_grid = min((lay.np_cap * a.H * (plan::DV / 16) + 63) & ~63, 4 * n_cu);

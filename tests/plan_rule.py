@@ -1,16 +1,17 @@
 """Host restatement of the load-balancing rule of the forward pass, used by the GPU tests
 to check the plan the device writes (piece length, pieces, split sequences).
 
-A sequence of n chunks is split when n > 9L/8: a first piece of L chunks, then
-ceil((n - L) / L) near-equal later pieces (each run as two chains).  L is the smallest
-length >= max(4, ceil(H S / n_cu)) with H (S + E(L)) <= n_cu L, where S is the total of
-chunks and E(L) the chunks moved into later pieces; L then grows by 1/16 steps while the
-units longer than L/2 outnumber the CUs.
+Chunks are cs tokens; n_slots chunk-kernel workgroups run at once.  A sequence of n
+chunks is split when n > 9L/8: a first piece of L chunks, then ceil((n - L) / L) near-equal
+later pieces (each run as two chains).  L is the smallest length >= max(4,
+ceil(H S / n_slots)) with H (S + E(L)) <= n_slots L, where S is the total of chunks and E(L)
+the chunks moved into later pieces; L then grows by 1/16 steps while the units longer
+than L/2 outnumber the slots.
 """
 
 
-def chunks(length):
-    return (length + 63) // 64 if length > 0 else 0
+def chunks(length, cs):
+    return (length + cs - 1) // cs if length > 0 else 0
 
 
 def split(n, L):
@@ -24,8 +25,9 @@ def later_pieces(n, L):
     return [base + (1 if i < rem else 0) for i in range(P)]
 
 
-def plan(lengths, H, n_cu, l_min=4):
-    n = [chunks(x) for x in lengths]
+def plan(lengths, H, n_slots, cs, l_min=4):
+    n_cu = n_slots
+    n = [chunks(x, cs) for x in lengths]
     S, maxn = sum(n), max(n) if n else 0
     L0 = max(l_min, (H * S + n_cu - 1) // n_cu)
     L = 0

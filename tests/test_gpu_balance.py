@@ -27,8 +27,12 @@ def _setup():
     build.build(force=False)
 
 
-def _n_cu():
-    return torch.cuda.get_device_properties(0).multi_processor_count
+# the forward pass runs 64-token chunks, one workgroup per CU
+CHUNK, PER_CU = 64, 1
+
+
+def _n_slots():
+    return PER_CU * torch.cuda.get_device_properties(0).multi_processor_count
 
 
 def _desc(w, inp):
@@ -64,7 +68,7 @@ def _header(h):
 
 def _check_plan(w, hdr):
     from plan_rule import plan
-    exp = plan(list(w.lengths), w.H, _n_cu())
+    exp = plan(list(w.lengths), w.H, _n_slots(), CHUNK)
     got = _header(hdr)
     print(f"  plan: expected {exp}, device {got}", flush=True)
     for key in ("L", "n_split", "n_piece", "n_echunk"):
