@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_chain.hip", "kda_decode.hip", "kda_fast.hip", "kda_fast32.hip", "kda_plan.hip", "kda_scan.hip"]
+SOURCES = ["kda_api.hip", "kda_chain.hip", "kda_decode.hip", "kda_fast.hip", "kda_plan.hip", "kda_scan.hip"]
 HEADERS = ["kda_common.h", "kda_fast_common.h", "kda_launch.h"]
 
 HIPCC_FLAGS = [

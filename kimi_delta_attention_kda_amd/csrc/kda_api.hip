@@ -174,8 +174,6 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
             if (st != KDA_OK) return st;
             if (workspace_bytes < need) return KDA_ERR_SHAPE;
             e = kda::launch_planned_fwd(a, (char *)workspace, lay, n_cu, fwd_kernel(), (hipStream_t)stream);
-        } else if (fwd_kernel().chunk == 32) {
-            e = kda::launch_fast32(a, (hipStream_t)stream);
         } else {
             e = kda::launch_fast(a, kda::MODE_FWD, (hipStream_t)stream);
         }

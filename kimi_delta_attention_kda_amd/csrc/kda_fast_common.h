@@ -1,5 +1,4 @@
-// kda_fast_common.h -- device helpers shared by the chunk kernels for dk = dv = 128
-// (kda_fast.hip: 64-token chunks, 8 waves; kda_fast32.hip: 32-token chunks, 4 waves).
+// kda_fast_common.h -- device helpers of the dk = dv = 128 chunk kernel (kda_fast.hip).
 #pragma once
 
 #include "kda_common.h"

@@ -78,10 +78,6 @@ hipError_t launch_chain(const ChainArgs &a, int dk, int dvs, bool precise, int m
 hipError_t launch_fast(const ChainArgs &a, int mode, hipStream_t stream);
 // forward pass over the queues of a plan (a.plan set), one persistent workgroup per CU
 hipError_t launch_fast_planned(const ChainArgs &a, int n_cu, hipStream_t stream);
-// bf16, dk = dv = 128 forward pass with 32-token chunks and 4-wave workgroups, two per CU:
-// one workgroup per (item, head), or persistent over a plan's queues (n_slots workgroups)
-hipError_t launch_fast32(const ChainArgs &a, hipStream_t stream);
-hipError_t launch_fast32_planned(const ChainArgs &a, int n_slots, hipStream_t stream);
 // The chunk kernel of the bf16 dk = dv = 128 forward pass: its chunk length and how many of
 // its workgroups share a CU (the planner sizes pieces in its chunks, for that many slots).
 struct FwdKernel {
@@ -89,7 +85,6 @@ struct FwdKernel {
     int per_cu;
 };
 constexpr FwdKernel FWD64 = {64, 1};  // kda_fast.hip
-constexpr FwdKernel FWD32 = {32, 2};  // kda_fast32.hip
 
 // Planner, piece-state scan and output correction of the load-balanced forward pass
 // (bf16, dk = dv = 128).  ws is the workspace laid out by plan_layout.

@@ -551,7 +551,7 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     a.ws_M = (float *)(ws + lay.M);
     a.ws_U = (float *)(ws + lay.U);
     a.ws_W = ws + lay.W;
-    e = fk.chunk == 32 ? launch_fast32_planned(a, fk.per_cu * n_cu, stream) : launch_fast_planned(a, n_cu, stream);
+    e = launch_fast_planned(a, fk.per_cu * n_cu, stream);
     if (e != hipSuccess) return e;
 
     plan::PieceArgs pp;
