@@ -143,13 +143,13 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 has_v = !isM;
             }
         } else {
-            if (t == 0) s_next = atomicAdd((int *)&a.plan->ctr[xcd], 1);
+            if (t == 0) s_next = atomicAdd((int *)&a.plan->ctr, 1);
             __syncthreads();
             // every value of the unit is wave-uniform: keep it in scalar registers
             const int u = __builtin_amdgcn_readfirstlane(s_next);
             __syncthreads();
-            if (u >= a.plan->qlen[xcd]) break;
-            const int2 qe = a.queue[xcd * a.qcap + u];
+            if (u >= a.plan->qlen) break;
+            const int2 qe = a.queue[u];
             const int qx = __builtin_amdgcn_readfirstlane(qe.x), qy = __builtin_amdgcn_readfirstlane(qe.y);
             if (qy < 0) continue;  // skip slot
             const int4 en = a.ent[qx];

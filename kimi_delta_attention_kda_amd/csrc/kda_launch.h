@@ -16,15 +16,15 @@ enum { MODE_FWD = 0, MODE_SUMMARY = 1 };
 enum { ROLE_WHOLE = 0, ROLE_M = 1, ROLE_U = 2 };
 
 struct PlanHeader {
-    int ctr[8];    // per-XCD queue cursors (atomics), zeroed by the planner
-    int qlen[8];   // per-XCD queue lengths, counting skip slots
+    int ctr;       // queue cursor (atomic), zeroed by the planner
+    int qlen;      // queue length, counting skip slots
     int n_split;   // sequences cut into pieces
     int n_piece;   // pieces after the first, over all split sequences
     int n_echunk;  // chunks in those pieces
     int L;         // first-piece length in chunks (0: nothing split)
     int n_ent;
     int n_sorted;
-    int pad[14];
+    int pad[28];
 };
 
 // Byte offsets of the parts of the forward-pass workspace.
@@ -32,7 +32,7 @@ struct PlanLayout {
     size_t hdr, queue, ent, piece, sseq, sorted, M, U, XT, W, total;
     int np_cap;   // capacity for pieces after the first
     int ent_cap;  // capacity for entities (sequences + pieces)
-    int qcap;     // capacity of one XCD queue (int2 entries)
+    int qcap;     // capacity of the queue (int2 entries)
 };
 PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_slots);
 
@@ -59,11 +59,10 @@ struct ChainArgs {
     float scale;
     int v_first;             // pool slots stored [dv][dk] (V_FIRST) instead of [dk][dv]
     // load-balanced forward pass: when plan is set, workgroups take units from the
-    // per-XCD queues instead of one (item, head) each
+    // planner's queue instead of one (item, head) each
     const PlanHeader *plan;
-    const int2 *queue;       // [8][qcap]: (entity, head | role << 16), head < 0 in skip slots
+    const int2 *queue;       // [qcap]: (entity, head | role << 16), head < 0 in skip slots
     const int4 *ent;         // entity: (sequence, first chunk, end chunk, piece or -1)
-    int qcap;
     float *ws_M;             // [n_piece][H][dk][dk]
     float *ws_U;             // [n_piece][H][dk][dv]
     void *ws_W;              // [T][H][dv] bf16, W rows of the later pieces

@@ -11,9 +11,9 @@
 // and both chains run without knowing X.  Per forward call:
 //   1. plan_kernel (one workgroup) chooses a first-piece length L, cuts every sequence
 //      longer than 9L/8 into a first piece of L chunks plus near-equal later pieces of at
-//      most L chunks, and deals the units, longest first, into eight per-XCD queues (the
-//      two chains of a later piece next to each other, so they share the XCD's L2);
-//   2. kda_fast_kernel drains the queues: whole sequences and first pieces run from the
+//      most L chunks, and lists the units, longest first, in one queue (the two chains of
+//      a later piece next to each other);
+//   2. kda_fast_kernel drains the queue: whole sequences and first pieces run from the
 //      pool slot as usual; a later piece runs its transition chain (W_t rows into the W
 //      buffer, final M) and its contribution chain (O_U rows into out, final U);
 //   3. piece_scan_kernel walks each split sequence's pieces in order: the incoming
@@ -49,7 +49,7 @@ struct PlanArgs {
     int4 *piece;   // (first token, end token, chunks, prefix of later-piece chunks)
     int4 *sseq;    // (sequence, first later piece, number of later pieces, pool slot)
     int *sorted;
-    int np_cap, ent_cap, qcap;
+    int np_cap, ent_cap;
 };
 
 __device__ __forceinline__ int chunks_of(const int32_t *cu, int b, int cs) {
@@ -290,24 +290,23 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
     }
     __syncthreads();
 
-    // ---- per-XCD queues: super unit s = (rank, head) goes to XCD s % 8, slots 2(s/8) and
-    // 2(s/8) + 1 (the contribution chain of a later piece, else a skip slot)
+    // ---- one queue for every workgroup: super unit s = (rank, head) takes slots 2s and
+    // 2s + 1 (the contribution chain of a later piece, else a skip slot). One queue packs
+    // the units over all CUs at once; per-XCD queues, which kept the two chains of a
+    // piece on one L2, measured slower (the second chain's re-read of k, q and the gates
+    // costs less than the coarser packing).
     const int64_t NS = (int64_t)n_sorted * H;
     for (int64_t s = t; s < NS; s += PT) {
         const int r = (int)(s / H), hh = (int)(s - (int64_t)r * H);
         const int e = ecached ? ssort[r] : p.sorted[r];
         const bool pair = ent_at(e).w >= 0;
-        const int x = (int)(s & 7);
-        const int64_t i = s >> 3;
-        int2 *q = p.queue + (int64_t)x * p.qcap + 2 * i;
+        int2 *q = p.queue + 2 * s;
         q[0] = make_int2(e, hh | ((pair ? ROLE_M : ROLE_WHOLE) << 16));
         q[1] = pair ? make_int2(e, hh | (ROLE_U << 16)) : make_int2(0, -1);
     }
-    if (t < 8) {
-        p.hdr->ctr[t] = 0;
-        p.hdr->qlen[t] = NS > t ? (int)(2 * ((NS - t + 7) / 8)) : 0;
-    }
     if (t == 0) {
+        p.hdr->ctr = 0;
+        p.hdr->qlen = (int)(2 * NS);
         p.hdr->n_split = tot_s;
         p.hdr->n_piece = tot_p;
         p.hdr->n_echunk = tot_e;
@@ -495,12 +494,12 @@ PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_slots) {
     // load); twice that plus slack
     y.np_cap = 2 * ((n_slots + H - 1) / H) + 2;
     y.ent_cap = B + y.np_cap;
-    y.qcap = (int)(2 * (((int64_t)y.ent_cap * H + 7) / 8) + 2);
+    y.qcap = (int)(2 * (int64_t)y.ent_cap * H);
     size_t o = 0;
     y.hdr = o;
     o = plan::align256(o + sizeof(PlanHeader));
     y.queue = o;
-    o = plan::align256(o + (size_t)8 * y.qcap * sizeof(int2));
+    o = plan::align256(o + (size_t)y.qcap * sizeof(int2));
     y.ent = o;
     o = plan::align256(o + (size_t)y.ent_cap * sizeof(int4));
     y.piece = o;
@@ -539,7 +538,6 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     pa.sorted = (int *)(ws + lay.sorted);
     pa.np_cap = lay.np_cap;
     pa.ent_cap = lay.ent_cap;
-    pa.qcap = lay.qcap;
     hipLaunchKernelGGL(plan::plan_kernel, dim3(1), dim3(plan::PT), 0, stream, pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -547,7 +545,6 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     a.plan = pa.hdr;
     a.queue = pa.queue;
     a.ent = pa.ent;
-    a.qcap = lay.qcap;
     a.ws_M = (float *)(ws + lay.M);
     a.ws_U = (float *)(ws + lay.U);
     a.ws_W = ws + lay.W;

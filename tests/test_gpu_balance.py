@@ -61,9 +61,9 @@ def _run_with_ws(w, inp, nbytes=None):
 
 
 def _header(h):
-    # PlanHeader: ctr[8], qlen[8], n_split, n_piece, n_echunk, L, n_ent, n_sorted
-    return {"qlen": [int(x) for x in h[8:16]], "n_split": int(h[16]), "n_piece": int(h[17]),
-            "n_echunk": int(h[18]), "L": int(h[19]), "n_ent": int(h[20]), "n_sorted": int(h[21])}
+    # PlanHeader: ctr, qlen, n_split, n_piece, n_echunk, L, n_ent, n_sorted
+    return {"ctr": int(h[0]), "qlen": int(h[1]), "n_split": int(h[2]), "n_piece": int(h[3]),
+            "n_echunk": int(h[4]), "L": int(h[5]), "n_ent": int(h[6]), "n_sorted": int(h[7])}
 
 
 def _check_plan(w, hdr):
@@ -74,10 +74,12 @@ def _check_plan(w, hdr):
     for key in ("L", "n_split", "n_piece", "n_echunk"):
         assert got[key] == exp[key], key
     assert got["n_ent"] == w.B + exp["n_piece"]
-    # every (entity of nonzero length, head) is queued once, its later pieces as pairs
+    # every (entity of nonzero length, head) is queued once, its later pieces as pairs;
+    # the chunk kernel's workgroups drew every slot and one past the end each
     n_nonzero = sum(1 for x in w.lengths if x > 0) + exp["n_piece"]
     assert got["n_sorted"] == n_nonzero
-    assert sum(got["qlen"]) == 2 * n_nonzero * w.H
+    assert got["qlen"] == 2 * n_nonzero * w.H
+    assert got["ctr"] == got["qlen"] + 8 * ((_n_slots() + 7) // 8)
 
 
 def _compare_all(w, inp, out, pool):
