@@ -6,8 +6,9 @@ scores, triangular inverse, W/U construction, inter-chunk state pass, output), w
 load-balancing workspace: a planner kernel, the chunk kernel (the whole hot path of
 every chain), and for sequences cut into pieces a piece-state scan and an output
 correction.  Inputs are seeded synthetic tensors already resident in HBM.  Prints one
-JSON line; the per-call time is taken with HIP events on the launch stream around the
-whole call (all four kernels).
+JSON line; the per-call time is taken with one pair of HIP events on the launch stream
+around the whole timed region (all four kernels of every call, divided by the number of
+calls).  Events between the calls would add ~7 us of idle GPU time to each call.
 
 Default workload: 8 sequences (lengths uniform in [1024, 8192], 32768 tokens), H=32,
 dk=dv=128, bf16 q/k/v/out, fp32 gates and state, safe gate (bound -5), 64-slot pool.
@@ -143,18 +144,17 @@ def main():
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
         step(out)
-        ev[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    kern_ms = ev0.elapsed_time(ev1) / args.steps
     tokens_s = w.T / (ms_step / 1e3)
 
     nbytes = algorithmic_bytes(w)

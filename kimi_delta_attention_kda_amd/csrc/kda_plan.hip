@@ -30,6 +30,7 @@ namespace kda {
 namespace plan {
 
 constexpr int PT = 1024;   // planner threads
+constexpr int PT_ONE = 64; // threads of the one-wave planner (at most 64 entities)
 constexpr int NBIN = 1024; // length bins of the longest-first order
 constexpr int L_MIN = 4;   // shortest first piece worth a split, in chunks
 constexpr int NCACHE = 4096;  // sequences whose chunk counts the planner keeps in LDS
@@ -57,30 +58,36 @@ __device__ __forceinline__ int chunks_of(const int32_t *cu, int b, int cs) {
     return len > 0 ? (len + cs - 1) / cs : 0;
 }
 
-// Sum / max over the workgroup; every thread gets the result.
+// Sum / max over the workgroup of NT threads; every thread gets the result.  With one
+// wave the lane exchanges suffice: no LDS, no barrier.
+template <int NT>
 __device__ int64_t block_sum(int64_t v, int64_t *red) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if constexpr (NT == 64) return v;
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     int64_t s = 0;
 #pragma unroll
-    for (int i = 0; i < PT / 64; ++i) s += red[i];
+    for (int i = 0; i < NT / 64; ++i) s += red[i];
     return s;
 }
+template <int NT>
 __device__ int block_max(int v, int64_t *red) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    if constexpr (NT == 64) return v;
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     int m = 0;
 #pragma unroll
-    for (int i = 0; i < PT / 64; ++i) m = max(m, (int)red[i]);
+    for (int i = 0; i < NT / 64; ++i) m = max(m, (int)red[i]);
     return m;
 }
 // Exclusive prefix sum over the threads of the workgroup; total returned in *tot.
+template <int NT>
 __device__ int block_excl_scan(int v, int64_t *red, int *tot) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int x = v;
@@ -89,12 +96,16 @@ __device__ int block_excl_scan(int v, int64_t *red, int *tot) {
         const int y = __shfl_up(x, o);
         if (lane >= o) x += y;
     }
+    if constexpr (NT == 64) {
+        *tot = __shfl(x, 63);
+        return x - v;
+    }
     __syncthreads();
     if (lane == 63) red[wv] = x;
     __syncthreads();
     int base = 0, all = 0;
 #pragma unroll
-    for (int i = 0; i < PT / 64; ++i) {
+    for (int i = 0; i < NT / 64; ++i) {
         const int r = (int)red[i];
         if (i < wv) base += r;
         all += r;
@@ -104,6 +115,7 @@ __device__ int block_excl_scan(int v, int64_t *red, int *tot) {
 }
 
 // Three exclusive prefix sums at once (one pair of barriers).
+template <int NT>
 __device__ void block_excl_scan3(int a, int b, int c, int64_t *red, int *ea, int *eb, int *ec, int *ta,
                                  int *tb, int *tc) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -117,9 +129,18 @@ __device__ void block_excl_scan3(int a, int b, int c, int64_t *red, int *ea, int
             z += z1;
         }
     }
+    if constexpr (NT == 64) {
+        *ea = x - a;
+        *eb = y - b;
+        *ec = z - c;
+        *ta = __shfl(x, 63);
+        *tb = __shfl(y, 63);
+        *tc = __shfl(z, 63);
+        return;
+    }
     __syncthreads();
     // per-wave totals: (x, y) packed in red, z in zred
-    __shared__ int zred[PT / 64];
+    __shared__ int zred[NT / 64];
     if (lane == 63) {
         red[wv] = (int64_t)(((uint64_t)(uint32_t)y << 32) | (uint32_t)x);
         zred[wv] = z;
@@ -127,7 +148,7 @@ __device__ void block_excl_scan3(int a, int b, int c, int64_t *red, int *ea, int
     __syncthreads();
     int bx = 0, by = 0, bz = 0, ax = 0, ay = 0, az = 0;
 #pragma unroll
-    for (int i = 0; i < PT / 64; ++i) {
+    for (int i = 0; i < NT / 64; ++i) {
         const uint64_t v = (uint64_t)red[i];
         const int vx = (int)(uint32_t)v, vy = (int)(uint32_t)(v >> 32), vz = zred[i];
         if (i < wv) {
@@ -147,30 +168,38 @@ __device__ void block_excl_scan3(int a, int b, int c, int64_t *red, int *ea, int
     *tc = az;
 }
 
-__global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
-    __shared__ int64_t red[PT / 64];
-    __shared__ int hist[NBIN];
-    __shared__ int sn[NCACHE];
-    __shared__ int4 sent[ECACHE];
-    __shared__ int ssort[ECACHE];
+// NT = PT: any plan.  NT = PT_ONE: one wave, for at most 64 entities (sequences plus
+// later pieces), whose reductions need no barrier and whose longest-first order is an
+// exact rank sort.
+template <int NT>
+__global__ __launch_bounds__(NT) void plan_kernel(PlanArgs p) {
+    constexpr bool ONE = NT == PT_ONE;
+    constexpr int NC = ONE ? PT_ONE : NCACHE, EC = ONE ? PT_ONE : ECACHE;
+    __shared__ int64_t red[NT / 64];
+    __shared__ int hist[ONE ? 1 : NBIN];
+    __shared__ int sn[NC];
+    __shared__ int4 sent[EC];
+    __shared__ int ssort[EC];
     const int t = threadIdx.x;
     const int B = p.B, H = p.H;
-    const bool cached = B <= NCACHE;
+    const bool cached = B <= NC;
+    // one wave: thread b owns sequence b throughout; its slot is fetched with the lengths
+    const int si_own = (ONE && t < B) ? p.state_indices[t] : 0;
     if (cached)
-        for (int b = t; b < B; b += PT) sn[b] = chunks_of(p.cu, b, p.cs);
+        for (int b = t; b < B; b += NT) sn[b] = chunks_of(p.cu, b, p.cs);
     __syncthreads();
     auto chunks = [&](int b) { return cached ? sn[b] : chunks_of(p.cu, b, p.cs); };
 
     // ---- chunk totals
     int64_t s_loc = 0;
     int m_loc = 0;
-    for (int b = t; b < B; b += PT) {
+    for (int b = t; b < B; b += NT) {
         const int n = chunks(b);
         s_loc += n;
         m_loc = max(m_loc, n);
     }
-    const int64_t S = block_sum(s_loc, red);
-    const int maxn = block_max(m_loc, red);
+    const int64_t S = block_sum<NT>(s_loc, red);
+    const int maxn = block_max<NT>(m_loc, red);
 
     // ---- first-piece length: smallest L >= average load with H (S + E(L)) <= n_cu L,
     // E(L) = chunks moved into later pieces (they run twice)
@@ -181,11 +210,11 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
         while (lo < hi) {  // uniform: every thread sees the same sums
             const int mid = lo + (hi - lo) / 2;
             int64_t e = 0;
-            for (int b = t; b < B; b += PT) {
+            for (int b = t; b < B; b += NT) {
                 const int n = chunks(b);
                 if (8 * (int64_t)n > 9 * (int64_t)mid) e += n - mid;
             }
-            const int64_t E = block_sum(e, red);
+            const int64_t E = block_sum<NT>(e, red);
             if ((int64_t)H * (S + E) <= (int64_t)p.n_cu * mid) hi = mid;
             else lo = mid + 1;
         }
@@ -194,7 +223,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
         // the CUs, lengthen the pieces (fewer, longer units).
         while (L < maxn) {
             int64_t big = 0;
-            for (int b = t; b < B; b += PT) {
+            for (int b = t; b < B; b += NT) {
                 const int n = chunks(b);
                 if (8 * (int64_t)n > 9 * (int64_t)L) {
                     const int R = n - L, P = (R + L - 1) / L, base = R / P, rem = R % P;
@@ -203,7 +232,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
                     big += 1;
                 }
             }
-            if ((int64_t)H * block_sum(big, red) <= p.n_cu) break;
+            if ((int64_t)H * block_sum<NT>(big, red) <= p.n_cu) break;
             L = max(L + 1, (int)((int64_t)L * 17 / 16));
         }
         if (!(8 * (int64_t)maxn > 9 * (int64_t)L)) L = 0;
@@ -211,7 +240,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
 
     // ---- pieces: each thread owns a contiguous range of sequences, so the later
     // pieces of one sequence get consecutive indices
-    const int per = (B + PT - 1) / PT;
+    const int per = (B + NT - 1) / NT;
     const int b0 = min(B, t * per), b1 = min(B, b0 + per);
     int my_p = 0, my_s = 0, my_e = 0;
     auto split_of = [&](int n) { return L > 0 && 8 * (int64_t)n > 9 * (int64_t)L; };
@@ -224,13 +253,13 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
         }
     }
     int tot_p, tot_s, tot_e, kb, jb, eb;
-    block_excl_scan3(my_p, my_s, my_e, red, &kb, &jb, &eb, &tot_p, &tot_s, &tot_e);
+    block_excl_scan3<NT>(my_p, my_s, my_e, red, &kb, &jb, &eb, &tot_p, &tot_s, &tot_e);
     if (tot_p > p.np_cap || B + tot_p > p.ent_cap) {  // cannot happen by the sizing; stay safe
         L = 0;
         tot_p = tot_s = tot_e = 0;
     }
     const int n_ent = B + tot_p;
-    const bool ecached = n_ent <= ECACHE;
+    const bool ecached = n_ent <= EC;
     auto put_ent = [&](int e, int4 v) {
         p.ent[e] = v;
         if (ecached) sent[e] = v;
@@ -240,7 +269,7 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
         const int n = chunks(b);
         if (split_of(n)) {
             const int R = n - L, P = (R + L - 1) / L, base = R / P, rem = R % P;
-            p.sseq[jb] = make_int4(b, kb, P, p.state_indices[b]);
+            p.sseq[jb] = make_int4(b, kb, P, ONE ? si_own : p.state_indices[b]);
             const int cb = p.cu[b], ce = p.cu[b + 1];
             int c = L;
             for (int i = 0; i < P; ++i) {
@@ -259,44 +288,58 @@ __global__ __launch_bounds__(PT) void plan_kernel(PlanArgs p) {
     }
     __syncthreads();
 
-    // ---- longest first: counting sort of the entities on 1024 length bins
-    int ml = 0;
-    for (int e = t; e < n_ent; e += PT) {
-        const int4 en = ent_at(e);
-        ml = max(ml, en.z - en.y);
-    }
-    const int maxlen = max(1, block_max(ml, red));
-    hist[t] = 0;
-    __syncthreads();
-    for (int e = t; e < n_ent; e += PT) {
-        const int4 en = ent_at(e);
-        const int len = en.z - en.y;
-        if (len > 0) atomicAdd(&hist[NBIN - 1 - (int)((int64_t)len * (NBIN - 1) / maxlen)], 1);
-    }
-    __syncthreads();
+    // ---- longest first
     int n_sorted;
-    const int start = block_excl_scan(hist[t], red, &n_sorted);
-    __syncthreads();
-    hist[t] = start;
-    __syncthreads();
-    for (int e = t; e < n_ent; e += PT) {
-        const int4 en = ent_at(e);
-        const int len = en.z - en.y;
-        if (len > 0) {
-            const int pos = atomicAdd(&hist[NBIN - 1 - (int)((int64_t)len * (NBIN - 1) / maxlen)], 1);
-            if (ecached) ssort[pos] = e;
-            else p.sorted[pos] = e;
+    if constexpr (ONE) {
+        // exact rank: entity e goes after every longer one and every equally long one
+        // with a smaller index (n_ent <= 64, all in LDS)
+        const int len = t < n_ent ? sent[t].z - sent[t].y : 0;
+        int rank = 0;
+        for (int f = 0; f < n_ent; ++f) {
+            const int lf = sent[f].z - sent[f].y;
+            rank += (lf > len || (lf == len && f < t)) ? 1 : 0;
         }
+        n_sorted = __popcll(__ballot(len > 0));
+        if (len > 0) ssort[rank] = t;
+        __syncthreads();
+    } else {
+        // counting sort of the entities on 1024 length bins
+        int ml = 0;
+        for (int e = t; e < n_ent; e += NT) {
+            const int4 en = ent_at(e);
+            ml = max(ml, en.z - en.y);
+        }
+        const int maxlen = max(1, block_max<NT>(ml, red));
+        hist[t] = 0;
+        __syncthreads();
+        for (int e = t; e < n_ent; e += NT) {
+            const int4 en = ent_at(e);
+            const int len = en.z - en.y;
+            if (len > 0) atomicAdd(&hist[NBIN - 1 - (int)((int64_t)len * (NBIN - 1) / maxlen)], 1);
+        }
+        __syncthreads();
+        const int start = block_excl_scan<NT>(hist[t], red, &n_sorted);
+        __syncthreads();
+        hist[t] = start;
+        __syncthreads();
+        for (int e = t; e < n_ent; e += NT) {
+            const int4 en = ent_at(e);
+            const int len = en.z - en.y;
+            if (len > 0) {
+                const int pos = atomicAdd(&hist[NBIN - 1 - (int)((int64_t)len * (NBIN - 1) / maxlen)], 1);
+                if (ecached) ssort[pos] = e;
+                else p.sorted[pos] = e;
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
-
     // ---- one queue for every workgroup: super unit s = (rank, head) takes slots 2s and
     // 2s + 1 (the contribution chain of a later piece, else a skip slot). One queue packs
     // the units over all CUs at once; per-XCD queues, which kept the two chains of a
     // piece on one L2, measured slower (the second chain's re-read of k, q and the gates
     // costs less than the coarser packing).
     const int64_t NS = (int64_t)n_sorted * H;
-    for (int64_t s = t; s < NS; s += PT) {
+    for (int64_t s = t; s < NS; s += NT) {
         const int r = (int)(s / H), hh = (int)(s - (int64_t)r * H);
         const int e = ecached ? ssort[r] : p.sorted[r];
         const bool pair = ent_at(e).w >= 0;
@@ -328,92 +371,99 @@ struct PieceArgs {
     bf16_t *out;
     int H;
     int v_first;    // pool slots stored [dv][dk]
-    int cs;         // tokens per chunk (a correction task covers one chunk)
+    int cs;         // tokens per chunk (a correction task covers one chunk, at most 64)
 };
 
 // Incoming states of the later pieces, in order, and the final state into the slot.
-// Task = (split sequence, head, 16-column block); thread t owns row t/2, 8 columns.
+// Task = (split sequence, head, 16-column block): X_{k+1} = M_k X_k + U_k on those
+// columns with fp32 16x16x4 MFMAs (products and sums in fp32, as the recurrence needs).
+// Wave w owns rows 32w .. 32w+31 (two 16-row tiles); lane (g, li) holds rows
+// 32w + 16tt + 4g + s of column li, the accumulator layout.  The contraction index of
+// MFMA step kk on lane quarter g is 32g + kk, so a lane's A operands are 32 consecutive
+// entries of one row of M_k (eight 16-byte loads) and its B operands one column of X_k
+// from LDS, skewed by 16 floats per 32 rows so the four quarters read distinct banks.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ int sx_at(int k, int c) { return 16 * k + c + 16 * (k >> 5); }
+
 __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
-    __shared__ float sx[DK][16];
-    const int t = threadIdx.x, H = p.H;
-    const int r = t >> 1, half = t & 1;
+    __shared__ float sx[16 * DK + 16 * (DK / 32)];
+    const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
+    const int H = p.H;
     const int n_tasks = p.hdr->n_split * H * (DV / 16);
     // The 8 column blocks of one (sequence, head) read the same M_k: keep them on one XCD
     // (workgroups are dealt to the XCDs round-robin), so M_k comes from HBM once.
     for (int lin = blockIdx.x; lin < ((n_tasks + 63) & ~63); lin += gridDim.x) {
         const int cb = (lin >> 3) & 7, jh = ((lin >> 6) << 3) | (lin & 7);
-        if (jh >= p.hdr->n_split * H) continue;
+        if (jh >= p.hdr->n_split * H) continue;  // uniform over the workgroup
         const int h = jh % H, j = jh / H;
         const int4 sq = p.sseq[j];
-        const int c0 = 16 * cb + 8 * half;
+        const int col = 16 * cb + li;
         float *slot = p.state_pool + ((int64_t)sq.w * H + h) * DK * DV;
-        float x[8];
-        if (p.v_first) {
+        // X_k of this lane: rows 32w + 16tt + 4g + s, column col
+        f32x4 x[2];
+        auto slot_at = [&](int r) -> float & { return p.v_first ? slot[col * DK + r] : slot[r * DV + col]; };
 #pragma unroll
-            for (int c = 0; c < 8; ++c) x[c] = slot[(c0 + c) * DK + r];
-        } else {
-            const f32x4 a0 = *(const f32x4 *)(slot + r * DV + c0), a1 = *(const f32x4 *)(slot + r * DV + c0 + 4);
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                x[c] = a0[c];
-                x[c + 4] = a1[c];
-            }
-        }
+            for (int s = 0; s < 4; ++s) x[tt][s] = slot_at(32 * w + 16 * tt + 4 * g + s);
         for (int i = 0; i < sq.z; ++i) {
             const int64_t kh = (int64_t)(sq.y + i) * H + h;
-            // the correction's MFMA reads X^T rows (one column of X) as bf16
-            bf16_t *xt = p.XT + kh * DV * DK + (int64_t)c0 * DK + r;
+            // M_k rows and U_k entries are independent of X_k: issue them first
+            f32x4 ma[2][8], acc[2];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) xt[c * DK] = (bf16_t)x[c];
-            __syncthreads();
+            for (int tt = 0; tt < 2; ++tt) {
+                const float *Mr = p.M + kh * DK * DK + (int64_t)(32 * w + 16 * tt + li) * DK + 32 * g;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) sx[r][8 * half + c] = x[c];
-            __syncthreads();
-            const float *Mr = p.M + kh * DK * DK + r * DK;
-            const float *Ur = p.U + kh * DK * DV + r * DV + c0;
-            // the whole row of M_k is loaded before the first FMA: one memory latency
-            f32x4 mrow[DK / 4];
+                for (int q = 0; q < 8; ++q) ma[tt][q] = *(const f32x4 *)(Mr + 4 * q);
+                const float *Ur = p.U + kh * DK * DV + (int64_t)(32 * w + 16 * tt + 4 * g) * DV + col;
 #pragma unroll
-            for (int q = 0; q < DK / 4; ++q) mrow[q] = *(const f32x4 *)(Mr + 4 * q);
-            const f32x4 u0 = *(const f32x4 *)Ur, u1 = *(const f32x4 *)(Ur + 4);
-            float y[8];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                y[c] = u0[c];
-                y[c + 4] = u1[c];
+                for (int s = 0; s < 4; ++s) acc[tt][s] = Ur[s * DV];
             }
-            // X_{k+1} = M_k X_k + U_k, fp32, keys in order
+            // the correction's MFMA reads X_k^T rows (one column of X_k) as bf16
+            bf16_t *xt = p.XT + kh * DV * DK + (int64_t)col * DK + 32 * w + 4 * g;
 #pragma unroll
-            for (int q = 0; q < DK / 4; ++q)
+            for (int tt = 0; tt < 2; ++tt) *(bf16x4 *)(xt + 16 * tt) = bf4(x[tt]);
+            __syncthreads();  // every wave is done reading the previous X from LDS
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) y[c] = fmaf(mrow[q][e], sx[4 * q + e][8 * half + c], y[c]);
+                for (int s = 0; s < 4; ++s) sx[sx_at(32 * w + 16 * tt + 4 * g + s, li)] = x[tt][s];
+            __syncthreads();
 #pragma unroll
-            for (int c = 0; c < 8; ++c) x[c] = y[c];
+            for (int q = 0; q < 8; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float bx = sx[sx_at(32 * g + 4 * q + e, li)];
+                    acc[0] = mfma_f32(ma[0][q][e], bx, acc[0]);
+                    acc[1] = mfma_f32(ma[1][q][e], bx, acc[1]);
+                }
+            x[0] = acc[0];
+            x[1] = acc[1];
         }
-        if (p.v_first) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) slot[(c0 + c) * DK + r] = x[c];
-        } else {
-            *(f32x4 *)(slot + r * DV + c0) = f32x4{x[0], x[1], x[2], x[3]};
-            *(f32x4 *)(slot + r * DV + c0 + 4) = f32x4{x[4], x[5], x[6], x[7]};
-        }
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) slot_at(32 * w + 16 * tt + 4 * g + s) = x[tt][s];
         __syncthreads();
     }
 }
 
 // out_t += W_t X_k for every token of every later piece.  Task = (piece, head, chunk),
-// numbered piece-major; a workgroup takes a contiguous share of tasks, decodes them from
-// the piece table staged once in LDS, and mostly reuses one X_k^T (bf16, written by
-// piece_scan_kernel), held as MFMA fragments in registers.  Wave w computes columns
-// 32w .. 32w+31 as C^T = X^T W^T (16x16x32 bf16 MFMA): each lane then adds 4 consecutive
-// columns of one token (one 8-byte read-modify-write).
-constexpr int FIX_NP = 1024;  // pieces staged in LDS (more: read from global memory)
-constexpr int FIX_TASKS = 4;  // tasks per workgroup
+// numbered piece-major; a workgroup takes FIX_TASKS consecutive tasks (mostly one piece
+// and head), decodes them from the piece table staged once in LDS, and stages X_k^T (bf16,
+// written by piece_scan_kernel) in LDS when the piece or head changes.  Wave w owns the
+// 16 tokens 16w .. 16w+15 of the chunk and all 128 columns, C^T = X^T W^T with 16x16x32
+// bf16 MFMAs: each W row is read once, and a lane adds 4 consecutive columns of one token
+// per column tile (8-byte read-modify-writes).
+constexpr int FIX_NP = 256;   // pieces staged in LDS (more: read from global memory)
+constexpr int FIX_XP = DK + 8;  // bf16 pitch of the staged X^T rows
+constexpr int FIX_TASKS = 4;    // tasks per group (1, 2 and 4 measured within 10% of each other)
 
 __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
     __shared__ int4 spc[FIX_NP];
+    __shared__ __attribute__((aligned(16))) bf16_t sxt[DV * FIX_XP];
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
     const int H = p.H;
     const int n_piece = p.hdr->n_piece;
@@ -425,7 +475,6 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
     __syncthreads();
     auto piece_at = [&](int i) { return staged ? spc[i] : p.piece[i]; };
     int cur = -1;
-    bf16x8 xa[2][4];
     // groups of FIX_TASKS consecutive tasks, strided over the grid
     for (int64_t grp = blockIdx.x; grp * FIX_TASKS < n_tasks; grp += gridDim.x)
     for (int64_t task = grp * FIX_TASKS; task < min(n_tasks, (grp + 1) * FIX_TASKS); ++task) {
@@ -442,44 +491,35 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         const int key = lo * H + h;
         const int t0 = pc.x + p.cs * c;
         const int n = min(p.cs, pc.y - t0);
-        // every load of the task first (rows past the end repeat the last row and are
-        // not stored), so the task waits for memory once
-        // (at most four 16-token tiles: chunks of 32 or 64 tokens)
-        bf16x8 bw[4][4];
-        bf16x4 ov[4][2];
+        // this wave's loads first; rows past the chunk's end repeat its last row and are
+        // not stored (a wave past the end of a short chunk only joins the barriers)
+        const int64_t rowh = (int64_t)(t0 + min(16 * w + li, n - 1)) * H + h;
+        bf16x8 bw[4];
+        bf16x4 ov[8];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            if (16 * tt >= p.cs) break;
-            // rows past the chunk's end repeat its last row and are not stored
-            const int64_t rowh = (int64_t)(t0 + min(16 * tt + li, n - 1)) * H + h;
+        for (int kb = 0; kb < 4; ++kb) bw[kb] = *(const bf16x8 *)(p.W + rowh * DV + 32 * kb + 8 * g);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) bw[tt][kb] = *(const bf16x8 *)(p.W + rowh * DV + 32 * kb + 8 * g);
-            ov[tt][0] = *(const bf16x4 *)(p.out + rowh * DV + 32 * w + 4 * g);
-            ov[tt][1] = *(const bf16x4 *)(p.out + rowh * DV + 32 * w + 16 + 4 * g);
-        }
-        if (key != cur) {
+        for (int ct = 0; ct < 8; ++ct) ov[ct] = *(const bf16x4 *)(p.out + rowh * DV + 16 * ct + 4 * g);
+        if (key != cur) {  // uniform over the workgroup
+            __syncthreads();  // every wave is done with the previous X^T
             const bf16_t *xt = p.XT + (int64_t)key * DV * DK;
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-                    xa[ct][kb] = *(const bf16x8 *)(xt + (32 * w + 16 * ct + li) * DK + 32 * kb + 8 * g);
+            for (int i = 0; i < DV * DK / (8 * 256); ++i) {
+                const int e = 8 * (t + 256 * i), r = e / DK, cc = e - r * DK;
+                *(bf16x8 *)(sxt + r * FIX_XP + cc) = *(const bf16x8 *)(xt + e);
+            }
+            __syncthreads();
             cur = key;
         }
+        const bool store = 16 * w + li < n;
+        bf16_t *o = p.out + ((int64_t)(t0 + 16 * w + li) * H + h) * DV + 4 * g;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            if (16 * tt >= p.cs) break;
-            f32x4 acc0 = f4(ov[tt][0]), acc1 = f4(ov[tt][1]);
+        for (int ct = 0; ct < 8; ++ct) {
+            f32x4 acc = f4(ov[ct]);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                acc0 = mfma(xa[0][kb], bw[tt][kb], acc0);
-                acc1 = mfma(xa[1][kb], bw[tt][kb], acc1);
-            }
-            if (16 * tt + li < n) {
-                bf16_t *o = p.out + ((int64_t)(t0 + 16 * tt + li) * H + h) * DV + 32 * w + 4 * g;
-                *(bf16x4 *)o = bf4(acc0);
-                *(bf16x4 *)(o + 16) = bf4(acc1);
-            }
+            for (int kb = 0; kb < 4; ++kb)
+                acc = mfma(*(const bf16x8 *)(sxt + (16 * ct + li) * FIX_XP + 32 * kb + 8 * g), bw[kb], acc);
+            if (store) *(bf16x4 *)(o + 16 * ct) = bf4(acc);
         }
     }
 }
@@ -538,7 +578,10 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     pa.sorted = (int *)(ws + lay.sorted);
     pa.np_cap = lay.np_cap;
     pa.ent_cap = lay.ent_cap;
-    hipLaunchKernelGGL(plan::plan_kernel, dim3(1), dim3(plan::PT), 0, stream, pa);
+    if (lay.ent_cap <= plan::PT_ONE)
+        hipLaunchKernelGGL(plan::plan_kernel<plan::PT_ONE>, dim3(1), dim3(plan::PT_ONE), 0, stream, pa);
+    else
+        hipLaunchKernelGGL(plan::plan_kernel<plan::PT>, dim3(1), dim3(plan::PT), 0, stream, pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
