@@ -62,8 +62,9 @@ struct Lds {
     static constexpr int F_KHL = F_KHH + DK * PJ * 2;                // Khat^T lo
     static constexpr int F_A = F_KHL + DK * PJ * 2;                  // A (f32)
     static constexpr int F_P = F_A + 64 * PF * 4;                    // P (bf16)
-    static constexpr int F_T = F_P + (FW ? 64 * PJ * 2 : 0);         // T = (I+A)^-1 (bf16)
-    static constexpr int F_VT = F_T + 64 * PJ * 2;                   // V^T slice (bf16)
+    static constexpr int F_T = F_P + (FW ? 64 * PJ * 2 : 0);         // T = (I+A)^-1, bf16 hi
+    static constexpr int F_TL = F_T + 64 * PJ * 2;                   // and lo
+    static constexpr int F_VT = F_TL + 64 * PJ * 2;                  // V^T slice (bf16)
     static constexpr int F_BETA = F_VT + DVS * PJ * 2;
     static constexpr int F_E = F_BETA + 64 * 4;                      // block decays [4][DK]
     static constexpr int F_PI = F_E + 4 * DK * 4;                    // e^{G_(16I-1)} [4][DK]
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
             bf16_t *sKHL = (bf16_t *)(smem + L::F_KHL);
             bf16_t *sP = (bf16_t *)(smem + L::F_P);
             bf16_t *sT = (bf16_t *)(smem + L::F_T);
+            bf16_t *sTL = (bf16_t *)(smem + L::F_TL);
             bf16_t *sVT = (bf16_t *)(smem + L::F_VT);
             float *sE = (float *)(smem + L::F_E);
             float *sPI = (float *)(smem + L::F_PI);
@@ -442,16 +444,28 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
             invert_unit_lower<PF>(sA, Tf, sX, t);
             for (int e = t; e < 64 * 64; e += NT) {
                 const int i = e >> 6, j = e & 63;
-                sT[i * PJ + j] = (bf16_t)Tf[i * PF + j];
+                const float x = Tf[i * PF + j];
+                const bf16_t hi = (bf16_t)x;
+                sT[i * PJ + j] = hi;
+                sTL[i * PJ + j] = (bf16_t)(x - (float)hi);
             }
             __syncthreads();
 
-            // ---- chain step for this wave's value tiles
-            bf16x8 Sb[NVT][NKB];
+            // ---- chain step for this wave's value tiles.  The prediction K S takes S as
+            // bf16 hi + lo: where a key channel barely decays, the rounding of S to bf16
+            // is not forgotten between chunks and accumulates to ~1e-3 of the state.  The
+            // output product uses the hi part.
+            bf16x8 Sb[NVT][NKB], Sl[NVT][NKB];
 #pragma unroll
             for (int m = 0; m < NVT; ++m)
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) Sb[m][kb] = cat(bf4(S[m][2 * kb]), bf4(S[m][2 * kb + 1]));
+                for (int kb = 0; kb < NKB; ++kb) {
+                    bf16x4 h0, l0, h1, l1;
+                    split4(S[m][2 * kb], h0, l0);
+                    split4(S[m][2 * kb + 1], h1, l1);
+                    Sb[m][kb] = cat(h0, h1);
+                    Sl[m][kb] = cat(l0, l1);
+                }
 
             f32x4 Y[NVT][4], Z[NVT][4];
 #pragma unroll
@@ -462,7 +476,10 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 for (int kb = 0; kb < NKB; ++kb) {
                     const bf16x8 aK = fragA_perm(sKR, PK, 16 * rt + li, 32 * kb, g);
 #pragma unroll
-                    for (int m = 0; m < NVT; ++m) Y[m][rt] = mfma(aK, Sb[m][kb], Y[m][rt]);
+                    for (int m = 0; m < NVT; ++m) {
+                        Y[m][rt] = mfma(aK, Sb[m][kb], Y[m][rt]);
+                        Y[m][rt] = mfma(aK, Sl[m][kb], Y[m][rt]);
+                    }
                     if (FW) {
                         const bf16x8 aQ = fragA_perm(sQR, PK, 16 * rt + li, 32 * kb, g);
 #pragma unroll
@@ -491,11 +508,14 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 for (int m = 0; m < NVT; ++m) Uacc[m] = zero4();
 #pragma unroll
                 for (int jb = 0; jb <= (rt >> 1); ++jb) {
+                    // T as bf16 hi + lo as well: its rounding, like that of S, is not
+                    // forgotten where a key channel barely decays
                     const bf16x8 aT = fragA_perm(sT, PJ, 16 * rt + li, 32 * jb, g);
+                    const bf16x8 aTl = fragA_perm(sTL, PJ, 16 * rt + li, 32 * jb, g);
 #pragma unroll
                     for (int m = 0; m < NVT; ++m)
-                        Uacc[m] = mma3(Uacc[m], aT, aT, cat(Rh[m][2 * jb], Rh[m][2 * jb + 1]),
-                                       cat(Rl[m][2 * jb], Rl[m][2 * jb + 1]), false, true);
+                        Uacc[m] = mma3(Uacc[m], aT, aTl, cat(Rh[m][2 * jb], Rh[m][2 * jb + 1]),
+                                       cat(Rl[m][2 * jb], Rl[m][2 * jb + 1]), true, true);
                 }
 #pragma unroll
                 for (int m = 0; m < NVT; ++m) split4(Uacc[m], Uh[m][rt], Ul[m][rt]);

@@ -458,6 +458,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
         // ============ chain step, first half: Y = Kg S, Z = S^T Qbar^T, R, forward substitution ============
         f32x4 Z[4];
         f16x4 Uh[4], Ul[4];
+        float usc, iusc;  // power-of-two scale of this wave's U and its inverse
         {
             bf16x8 Sb[4];
 #pragma unroll
@@ -475,13 +476,50 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                         Z[rt] = mfma(Sb[kb], *(const bf16x8 *)(sQB + (16 * rt + li) * PK + 32 * kb + 8 * g), Z[rt]);
                 }
             }
+            // The rounding of S to bf16 in the prediction Kg S is forgotten with the state
+            // when the chunk decays it, but accumulates to ~1e-3 of the state where a key
+            // channel barely decays.  Chunks in which some channel keeps more than 1/16 of
+            // its state over the chunk add the product with the rounding residual of S.
+            if (wave_max_nonneg(fmaxf(sEG[l], sEG[l + 64])) > 0x1p-4f) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const bf16x8 sh = Sb[kb];
+                    const bf16x8 sl = cat(bf4(S[2 * kb] - f4(bf16x4{sh[0], sh[1], sh[2], sh[3]})),
+                                          bf4(S[2 * kb + 1] - f4(bf16x4{sh[4], sh[5], sh[6], sh[7]})));
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt)
+                        Y[rt] = mfma(*(const bf16x8 *)(sKG + (16 * rt + li) * PK + 32 * kb + 8 * g), sl, Y[rt]);
+                }
+            }
             // R = beta (V - Kg S); solve (I + A) U = R block by block
             const int vcol = 16 * w + li;
+            float rmax = 0.f;
 #pragma unroll
             for (int bI = 0; bI < 4; ++bI) {
                 const f32x4 vv = f4(*(const bf16x4 *)(sVT + vcol * PJ + 16 * bI + 4 * g));
                 const f32x4 bb = *(const f32x4 *)(sBeta + 16 * bI + 4 * g);
-                f32x4 acc = bb * (vv - Y[bI]);
+                Y[bI] = bb * (vv - Y[bI]);
+                rmax = fmaxf(rmax, fmaxf(fmaxf(fabsf(Y[bI][0]), fabsf(Y[bI][1])), fmaxf(fabsf(Y[bI][2]), fabsf(Y[bI][3]))));
+            }
+            // U is carried as fp16 hi + lo, exact to ~2^-22 of its largest entry only while
+            // that entry is near 1: a wave whose R is small (tiny beta and a vanished state)
+            // scales R, hence U, by a power of two, undone exactly in the output scale and
+            // the state update below.
+            rmax = wave_max_nonneg(rmax);
+            if (rmax < 0x1p-8f && rmax > 0.f) {
+                // 2^k with rmax 2^k in [1/4, 1/2)
+                const int k = min(64, -2 - ((int)(__builtin_bit_cast(unsigned, rmax) >> 23) - 127));
+                usc = __builtin_bit_cast(float, (k + 127) << 23);
+                iusc = __builtin_bit_cast(float, (127 - k) << 23);
+#pragma unroll
+                for (int bI = 0; bI < 4; ++bI) Y[bI] *= usc;
+            } else {
+                usc = 1.f;
+                iusc = 1.f;
+            }
+#pragma unroll
+            for (int bI = 0; bI < 4; ++bI) {
+                f32x4 acc = Y[bI];
 #pragma unroll
                 for (int bJ = 0; bJ < bI; ++bJ) {
                     const f16x4 ao = *(const f16x4 *)(sAO + (16 * bI + li) * PJ + 16 * bJ + 4 * g);
@@ -502,6 +540,10 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
         // interleaved with the gate and decay products of chunk ck + 1 ============
         {
             if (FW) {
+                if (usc != 1.f)
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) Z[rt] *= usc;
+                const float osc = a.scale * iusc;
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     // O^T += U^T P^T
@@ -513,13 +555,16 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                     const int i = 16 * rt + li;
                     if (i < n)
                         *(bf16x4 *)(obase + ((int64_t)t0 * H + h) * DV + (unsigned)(i * (H * DV) + 16 * w + 4 * g)) =
-                            bf4(a.scale * Z[rt]);
+                            bf4(osc * Z[rt]);
                 }
             }
             // unconditional, so that it shares a basic block with the state update: past the
             // last chunk every row is padding and nothing it writes is read again
             prep0(ck + 1);
             // S <- Diag(e^{G_last}) S + Khat^T U
+            if (usc != 1.f)
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) S[ct] *= usc;
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) {
                 S[ct] *= *(const f32x4 *)(sEG + key_row(ct, 4 * g));
@@ -530,6 +575,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                     S[ct] = mfma32h(kh, cath(Ul[2 * jb], Ul[2 * jb + 1]), S[ct]);
                 }
             }
+            if (usc != 1.f)
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) S[ct] *= iusc;
         }
         if (ck + 2 < n_chunks) {
             issue(ck + 2, 0);

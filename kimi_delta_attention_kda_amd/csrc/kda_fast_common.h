@@ -61,10 +61,34 @@ __device__ __forceinline__ float gate_alpha(float raw, float dtb_l2e, float negA
     return fmaxf(a, amin);
 }
 
+// compile-time integer (template arguments of lambdas)
+template <int N>
+struct IC {
+    static constexpr int value = N;
+};
+
 // value held by lane q of this lane's quad (DPP quad permutation [q, q, q, q])
 template <int Q>
 __device__ __forceinline__ float quad_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), Q * 0x55, 0xF, 0xF, false));
+}
+
+// Maximum of a non-negative float over the wave, in a scalar register: lane exchanges
+// inside each row of 16 lanes (DPP, no LDS round trip), then the four row maxima read
+// into scalar registers, where non-negative floats order like their bit patterns.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    auto dpp_max = [](float v, auto ctrl) {
+        const int m = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), decltype(ctrl)::value, 0xF, 0xF, false);
+        return fmaxf(v, __builtin_bit_cast(float, m));
+    };
+    x = dpp_max(x, IC<0xB1>{});   // quad_perm [1,0,3,2]
+    x = dpp_max(x, IC<0x4E>{});   // quad_perm [2,3,0,1]
+    x = dpp_max(x, IC<0x141>{});  // row_half_mirror
+    x = dpp_max(x, IC<0x140>{});  // row_mirror
+    const unsigned b = __builtin_bit_cast(unsigned, x);
+    const unsigned m = max(max(__builtin_amdgcn_readlane(b, 0), __builtin_amdgcn_readlane(b, 16)),
+                           max(__builtin_amdgcn_readlane(b, 32), __builtin_amdgcn_readlane(b, 48)));
+    return __builtin_bit_cast(float, m);
 }
 
 // Step K of the quad-parallel unit-lower substitution (and the following steps): broadcast

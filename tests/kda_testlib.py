@@ -46,18 +46,24 @@ def rel_fro(S, S_ref):
     return float(np.linalg.norm(S - S_ref) / den) if den > 0 else float(np.linalg.norm(S))
 
 
-def compare_items(w, inp, out, pool, items, nthreads=None):
-    """Returns (worst output error, worst state error) over the sampled items."""
+def compare_items(w, inp, out, pool, items, nthreads=None, detail=False):
+    """Returns (worst output error, worst state error) over the sampled items, plus the
+    per-item errors when detail is set.  The final state is compared with the oracle's
+    state rounded to fp32, the precision of the pool: a state that has decayed below
+    fp32's range is zero there, and the kernel's must be too (rel_fro is then the
+    absolute norm)."""
     ref = oracle_items(w, inp, items, nthreads)
     worst_o, worst_s = 0.0, 0.0
+    per = []
     for (b, h), (o_ref, S_ref) in zip(items, ref):
         a, e = inp["cu"][b], inp["cu"][b + 1]
         o = wl.as_f64(out[a:e, h])
         S = wl.as_f64(pool[inp["indices"][b], h])
-        if e > a:
-            worst_o = max(worst_o, rel_out(o, o_ref))
-        worst_s = max(worst_s, rel_fro(S, S_ref))
-    return worst_o, worst_s
+        eo = rel_out(o, o_ref) if e > a else 0.0
+        es = rel_fro(S, S_ref.astype(np.float32).astype(np.float64))
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+        per.append(((b, h), eo, es))
+    return (worst_o, worst_s, per) if detail else (worst_o, worst_s)
 
 
 def untouched_slots_identical(inp, pool_after):

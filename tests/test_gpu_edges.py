@@ -1,0 +1,120 @@
+"""GPU parity at the edges of the input space.
+
+- Extreme gates on the bf16 path (safe gate): every alpha at the bound e^-5, where a
+  16-row block decays by e^-80 and its reciprocal e^80 enters the diagonal scores; alpha
+  = 1 (no decay); both in one chunk on alternate key channels; beta near 0 and near 1.
+- The same on the fp32 path with the original gate, where decays go far below e^-5 per
+  token.
+- No decay at all over 4,000 tokens (the steady level of the state's rounding error).
+- Many short sequences around a few long ones: more sequences than the planner keeps in
+  LDS (its global-memory paths), with pieces, against the oracle on samples.
+- No tokens: a batch of empty sequences leaves the pool untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_kda_amd as kda
+from kimi_delta_attention_kda_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from oracle import build
+    build.build(force=False)
+
+
+def _extreme_inputs(w):
+    """Sequence 0: alpha at the floor; 1: alpha = 1; 2: both, on alternate key channels and
+    swapped every 64 tokens; 3: beta ~ 0; 4: beta ~ 1 (alpha drawn as usual in 3 and 4)."""
+    inp = wl.make_inputs(w, "cuda")
+    cu = inp["cu"]
+    rg, bl = inp["raw_gate"], inp["beta_logits"]
+    rg[cu[0]:cu[1]] = 30.0
+    rg[cu[1]:cu[2]] = -30.0
+    a, e = cu[2], cu[3]
+    tok = torch.arange(e - a, device="cuda").view(-1, 1, 1)
+    ch = torch.arange(w.dk, device="cuda").view(1, 1, -1)
+    flip = ((tok // 64) + ch) % 2 == 0
+    rg[a:e] = torch.where(flip, 30.0, -30.0).expand(e - a, w.H, w.dk)
+    bl[cu[3]:cu[4]] = -30.0
+    bl[cu[4]:cu[5]] = 30.0
+    return inp
+
+
+@pytest.mark.parametrize("dtype,dk,gate", [("bf16", 128, 1), ("bf16", 64, 1), ("f32", 64, 0), ("f32", 64, 1)])
+def test_extreme_gates_against_oracle(dtype, dk, gate):
+    from kda_testlib import compare_items, run_fwd, untouched_slots_identical
+    from kda_testlib import OUT_TOL_BF16, OUT_TOL_F32, STATE_TOL
+    w = wl.custom([200, 200, 333, 150, 150], H=2, dk=dk, dv=dk, dtype=dtype, gate_mode=gate, seed=11)
+    print(f"[case] extreme gates {dtype} dk={dk} gate_mode={gate}", flush=True)
+    inp = _extreme_inputs(w)
+    out, pool = run_fwd(w, inp)
+    assert torch.isfinite(out.float()).all()
+    eo, es, per = compare_items(w, inp, out, pool, [(b, h) for b in range(w.B) for h in range(w.H)],
+                                detail=True)
+    for (b, h), e1, e2 in per:
+        print(f"  sequence {b} head {h}: out_err={e1:.3e} state_err={e2:.3e}", flush=True)
+    assert eo <= (OUT_TOL_BF16 if dtype == "bf16" else OUT_TOL_F32)
+    assert es <= STATE_TOL
+    assert untouched_slots_identical(inp, pool)
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_no_decay_long_against_oracle(dk):
+    """alpha = 1 for 4,000 tokens: nothing forgets the rounding of the state in the chunk
+    products, so its error reaches a steady level that the tolerance must cover."""
+    from kda_testlib import compare_items, run_fwd, OUT_TOL_BF16, STATE_TOL
+    w = wl.custom([4000, 1000], H=2, dk=dk, dv=dk, dtype="bf16", gate_mode=1, seed=14)
+    print(f"[case] no decay, 4000 and 1000 tokens, dk={dk}", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+    inp["raw_gate"].fill_(-30.0)
+    out, pool = run_fwd(w, inp)
+    eo, es, per = compare_items(w, inp, out, pool, [(b, h) for b in range(w.B) for h in range(w.H)],
+                                detail=True)
+    for (b, h), e1, e2 in per:
+        print(f"  sequence {b} head {h}: out_err={e1:.3e} state_err={e2:.3e}", flush=True)
+    assert eo <= OUT_TOL_BF16 and es <= STATE_TOL
+
+
+def test_many_sequences_with_pieces():
+    """5,000 short sequences and 4 long ones (H = 2): the planner's uncached paths, pieces
+    of the long sequences, and the single queue of 10,000+ units."""
+    from kda_testlib import compare_items, run_fwd, untouched_slots_identical, OUT_TOL_BF16, STATE_TOL
+    rng = np.random.default_rng(7)
+    short = rng.integers(1, 41, size=5000).tolist()
+    lengths = [8000] + short[:2500] + [8000, 7000] + short[2500:] + [6000]
+    w = wl.custom(lengths, H=2, dk=128, dv=128, dtype="bf16", gate_mode=1, seed=12)
+    print(f"[case] many sequences B={w.B} T={w.T}", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+    out, pool = run_fwd(w, inp)
+    assert untouched_slots_identical(inp, pool)
+    longs = [i for i, n in enumerate(lengths) if n >= 6000]
+    picks = sorted(set(longs) | set(rng.choice(w.B, size=40, replace=False).tolist()))
+    items = [(b, h) for b in picks for h in range(w.H)]
+    eo, es = compare_items(w, inp, out, pool, items)
+    print(f"  {len(items)} sampled pairs: out_err={eo:.3e} state_err={es:.3e}", flush=True)
+    assert eo <= OUT_TOL_BF16 and es <= STATE_TOL
+    # the unbalanced launch agrees (the balanced one splits the long sequences)
+    out_n, pool_n = run_fwd(w, inp, workspace="none")
+    from kda_testlib import rel_out, rel_fro
+    for b in longs:
+        a, e = inp["cu"][b], inp["cu"][b + 1]
+        s = inp["indices"][b]
+        assert rel_out(wl.as_f64(out[a:e]), wl.as_f64(out_n[a:e])) <= OUT_TOL_BF16
+        assert rel_fro(wl.as_f64(pool[s]), wl.as_f64(pool_n[s])) <= STATE_TOL
+
+
+@pytest.mark.parametrize("workspace", ["torch", "none"])
+def test_no_tokens(workspace):
+    from kda_testlib import run_fwd
+    w = wl.custom([0, 0, 0], H=2, dk=128, dv=128, dtype="bf16", gate_mode=1, seed=13)
+    print(f"[case] three empty sequences, workspace={workspace}", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+    out, pool = run_fwd(w, inp, workspace=workspace)
+    assert out.shape == (0, w.H, w.dv)
+    assert torch.equal(pool.view(torch.int32), inp["state_pool"].view(torch.int32))
