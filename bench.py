@@ -28,7 +28,21 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA prefill tokens/s at H=32 dk=dv=128 bf16, 32K tokens; % MFMA peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_varlen_32k_traffic.json")
+TRAFFIC_FILES = {"varlen_32k": os.path.join(ROOT, "profiles", "kda_chunk_fwd_varlen_32k_traffic.json"),
+                 "decode_512": os.path.join(ROOT, "profiles", "kda_decode_kernel_decode_512_traffic.json")}
+
+
+def measured_traffic(w):
+    """Calibrated HBM bytes per call from the counter summary of this workload, while the
+    kernel sources still hash to the measured version; else None."""
+    f = TRAFFIC_FILES.get(w.name)
+    if not f or not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        tr = json.load(fh)
+    if tr.get("kernel_source_sha") == kernel_source_sha() and tr.get("workload") == w.name:
+        return tr.get("hbm_bytes_per_call")
+    return None
 
 
 def kernel_source_sha() -> str:
@@ -56,6 +70,15 @@ def algorithmic_flops(w) -> int:
 
 def dense_tile_flops(w) -> int:
     return w.T * w.H * (2 * 64 * (3 * w.dk + 2 * w.dv) + 6 * w.dk * w.dv)
+
+
+def decode_bytes(w) -> int:
+    """Compulsory HBM bytes of one decode call: each (sequence, head) reads and writes its
+    fp32 state once and reads one token's q, k, v, gate pre-activations and beta logit,
+    writing one output row."""
+    e = 2 if w.dtype == "bf16" else 4
+    per_seq_head = 2 * w.dk * w.dv * 4 + (2 * w.dk + w.dv) * e + w.dv * e + w.dk * 4 + 4
+    return w.B * w.H * per_seq_head + w.H * (w.dk + 1) * 4 + w.B * 4
 
 
 def cpu_baseline(w, inp, target_s=12.0):
@@ -105,7 +128,9 @@ def main():
 
     w = wl.workload(args.workload)
     if w.segments:
-        raise SystemExit("bench.py times kda_chunk_fwd workloads")
+        raise SystemExit("bench.py times kda_chunk_fwd and kda_decode workloads")
+    if w.name.startswith("decode"):
+        return run_decode(args, w)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     print(f"[bench] workload={w.name} T={w.T} B={w.B} H={w.H} dk={w.dk} dv={w.dv} dtype={w.dtype}",
@@ -121,13 +146,7 @@ def main():
               file=sys.stderr, flush=True)
 
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print("[bench] copy calibration: 3 x 1 GiB read + 1 GiB write", file=sys.stderr, flush=True)
-        del src, dst
+        copy_calibration(dev)
 
     pool = inp["state_pool"]
     gate = "safe" if w.gate_mode == 1 else "original"
@@ -159,12 +178,7 @@ def main():
 
     nbytes = algorithmic_bytes(w)
     achieved = nbytes / (kern_ms / 1e3) / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_sha") == kernel_source_sha() and tr.get("workload") == w.name:
-            traffic = tr.get("hbm_bytes_per_launch")
+    traffic = measured_traffic(w)
     fl = algorithmic_flops(w)
     fl_dense = dense_tile_flops(w)
     rec = {
@@ -183,6 +197,87 @@ def main():
                  "frac_of_bf16_peak": round(fl / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "dense_tile_frac_of_bf16_peak": round(fl_dense / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "flops_per_launch_algorithmic": fl},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def copy_calibration(dev):
+    """A plain 1 GiB device copy, three times: the counter runs scale HBM byte counters
+    by what they read for it."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("[bench] copy calibration: 3 x 1 GiB read + 1 GiB write", file=sys.stderr, flush=True)
+
+
+def run_decode(args, w):
+    """kda_decode of one token per sequence (every sequence of the workload has length 1)."""
+    import torch
+    import kimi_delta_attention_kda_amd as kda
+    from kimi_delta_attention_kda_amd import workloads as wl
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload={w.name} B={w.B} H={w.H} dk={w.dk} dv={w.dv} dtype={w.dtype}",
+          file=sys.stderr, flush=True)
+    inp = wl.make_inputs(w, dev)
+    torch.cuda.synchronize()
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import build as obuild
+        from oracle import oracle as orc
+        obuild.build(force=False)
+        nth = orc.default_threads()
+        items = [(b, h) for b in range(w.B) for h in range(w.H)]
+        its = [orc.item_from_inputs(inp, b, h) for (b, h) in items]
+        t = time.perf_counter()
+        orc.forward_items(its, w.dk, w.dv, w.gate_mode, w.lower_bound, w.beta_mode, w.scale, nthreads=nth)
+        dt = time.perf_counter() - t
+        cpu = {"value": w.B / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+               "sample": f"the whole call: {w.B} sequences x {w.H} heads, one token each ({dt:.2f} s)"}
+    if args.copy_calibration:
+        copy_calibration(dev)
+    gate = "safe" if w.gate_mode == 1 else "original"
+    pool = inp["state_pool"]
+    out = torch.empty((w.B, w.H, w.dv), dtype=inp["q"].dtype, device=dev)
+
+    def step():
+        kda.decode(inp["q"], inp["k"], inp["v"], inp["raw_gate"], inp["beta_logits"], inp["a_log"],
+                   inp["dt_bias"], pool, inp["state_indices"], gate_mode=gate, lower_bound=w.lower_bound,
+                   scale=w.scale, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    nbytes = decode_bytes(w)
+    achieved = nbytes / (kern_ms / 1e3) / 1e9
+    rec = {
+        "metric": "KDA decode tokens/s (one token per sequence), H=32 dk=dv=128 bf16, 512 sequences",
+        "value": round(w.B / (ms_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "sequences": w.B, "heads": w.H, "dk": w.dk, "dv": w.dv,
+                   "gate": gate, "gate_lower_bound": w.lower_bound, "pool_slots": w.n_slots},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
+                     "kernel": "kda_decode_kernel", "kernel_ms": round(kern_ms, 4),
+                     "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

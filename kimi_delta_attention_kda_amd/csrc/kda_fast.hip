@@ -327,8 +327,10 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
                 for (int r = 0; r < 4; ++r) v4[r] = pv[r][cc];
                 *(bf16x4 *)(sVT + (c0 + cc) * PJ + rbase) = v4;
             }
-            // every wave holds the 64 beta logits of the chunk (identical stores)
-            sBeta[l] = l < n ? (a.beta_mode == 0 ? 1.f / (1.f + __expf(-pbl)) : pbl) : 0.f;
+            // every wave holds the 64 betas of the chunk (identical stores); the hardware
+            // reciprocal, not an IEEE division, and selects rather than a branch
+            const float sig = __builtin_amdgcn_rcpf(1.f + __expf(-pbl));
+            sBeta[l] = l < n ? (a.beta_mode == 0 ? sig : pbl) : 0.f;
         }
     };
     if (n_chunks > 0) {

@@ -91,10 +91,13 @@ def workload(name: str, seed: int = 0) -> Workload:
         L = tuple(int(v) for v in rng.integers(16, 2049, size=512))
         return Workload(name, L, 32, 128, 128, "bf16", 1, beta_sigma=2.0,
                         n_slots=1024, state_sigma=0.01, seed=seed)
+    if name == "decode_512":  # one token for each of 512 sequences (single-token decode)
+        return Workload(name, (1,) * 512, 32, 128, 128, "bf16", 1, n_slots=1024, state_sigma=0.01,
+                        seed=seed)
     raise KeyError(name)
 
 
-NAMES = ("tiny_fp32", "varlen_32k", "long_131k", "segments_262k", "short_varlen_512")
+NAMES = ("tiny_fp32", "varlen_32k", "long_131k", "segments_262k", "short_varlen_512", "decode_512")
 
 
 def custom(lengths, H=2, dk=64, dv=64, dtype="bf16", gate_mode=1, n_slots=None,
