@@ -1,0 +1,48 @@
+"""CPU checks of bench.py's roofline denominators and its one-GPU contract.
+
+The compulsory bytes and algorithmic flops of a call are restated here from their parts
+(every input read once, every output written once, each used pool slot read and written
+once; the chunk form's triangle-aware flop count), so a slip in bench.py's formulas shows.
+"""
+import os
+import subprocess
+import sys
+
+import bench
+from kimi_delta_attention_kda_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_prefill_compulsory_bytes_varlen_32k():
+    w = wl.workload("varlen_32k")
+    assert (w.T, w.B, w.H, w.dk, w.dv) == (32768, 8, 32, 128, 128)
+    per_token = w.H * (3 * 128 * 2 + 128 * 4 + 4 + 128 * 2)  # q k v bf16, raw f32, beta, out bf16
+    assert per_token == 49280
+    slots = 8 * 2 * (32 * 128 * 128 * 4)                     # 8 slots of 2 MiB, read and written
+    small = 32 * (128 + 1) * 4 + 9 * 4 + 8 * 4                # dt_bias, a_log, cu_seqlens, indices
+    assert bench.algorithmic_bytes(w) == 32768 * per_token + slots + small == 1648378052
+
+
+def test_prefill_algorithmic_flops_varlen_32k():
+    w = wl.workload("varlen_32k")
+    # per token-head: A, P, W at C dk; U~ and PU at C dv; W S, Qbar S, Khat^T U at 2 dk dv
+    per = 3 * 64 * 128 + 2 * 64 * 128 + 3 * 2 * 128 * 128
+    assert per == 139264
+    assert bench.algorithmic_flops(w) == 32768 * 32 * per
+    assert round(bench.algorithmic_flops(w) / 1e9, 1) == 146.0
+
+
+def test_decode_compulsory_bytes():
+    w = wl.workload("decode_512")
+    assert (w.B, w.T, w.H, w.dk, w.dv) == (512, 512, 32, 128, 128)
+    per = 2 * 128 * 128 * 4 + 3 * 128 * 2 + 128 * 2 + 128 * 4 + 4  # state r+w, q k v, out, raw, beta
+    assert bench.decode_bytes(w) == 512 * 32 * per + 32 * 129 * 4 + 512 * 4
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
