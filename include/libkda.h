@@ -30,7 +30,12 @@
  * or a combination outside the supported contract).  Data-dependent
  * preconditions (cu_seqlens monotone, state_indices in range and distinct)
  * are not checked by the asynchronous calls; kda_validate_varlen checks them
- * synchronously.  KDA_ERR_HIP reports a failed kernel launch.
+ * synchronously.  With the environment variable KDA_DEBUG_VALIDATE=1 the
+ * calls themselves first synchronise their stream and run the same checks
+ * (segment offsets for kda_segment_summary, slot indices for kda_decode),
+ * returning KDA_ERR_DATA before any launch on a violation; this is for
+ * debugging only, since it stalls the caller.  KDA_ERR_HIP reports a failed
+ * kernel launch.
  */
 #ifndef LIBKDA_H
 #define LIBKDA_H
@@ -51,7 +56,7 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = 4, /* valid but outside the supported contract           */
     KDA_ERR_ARG = 5,         /* bad mode value or scalar                           */
     KDA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed         */
-    KDA_ERR_DATA = 7         /* kda_validate_varlen: cu_seqlens / indices invalid  */
+    KDA_ERR_DATA = 7         /* cu_seqlens / offsets / indices invalid (validation) */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;

@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <cstdlib>
 #include <vector>
 
 #include "../../include/libkda.h"
@@ -137,6 +138,49 @@ kda_status check_fwd(const kda_desc *desc, const void *q, const void *k, const v
     return KDA_OK;
 }
 
+// Host checks of the data-dependent preconditions (synchronous copies to the host).
+kda_status check_offsets(const int32_t *offsets, int32_t n, int64_t total) {
+    std::vector<int32_t> cu(n + 1);
+    if (hipMemcpy(cu.data(), offsets, sizeof(int32_t) * (n + 1), hipMemcpyDeviceToHost) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (cu[0] != 0 || (int64_t)cu[n] != total) return KDA_ERR_DATA;
+    for (int b = 0; b < n; ++b)
+        if (cu[b + 1] < cu[b]) return KDA_ERR_DATA;
+    return KDA_OK;
+}
+
+kda_status check_indices(const int32_t *indices, int32_t n, int32_t max_slots) {
+    if (n == 0) return KDA_OK;
+    std::vector<int32_t> idx(n);
+    if (hipMemcpy(idx.data(), indices, sizeof(int32_t) * n, hipMemcpyDeviceToHost) != hipSuccess)
+        return KDA_ERR_HIP;
+    std::vector<char> seen(max_slots, 0);
+    for (int b = 0; b < n; ++b) {
+        if (idx[b] < 0 || idx[b] >= max_slots || seen[idx[b]]) return KDA_ERR_DATA;
+        seen[idx[b]] = 1;
+    }
+    return KDA_OK;
+}
+
+// With KDA_DEBUG_VALIDATE=1 in the environment the asynchronous calls first wait for
+// their stream and check the data-dependent preconditions; a violation returns
+// KDA_ERR_DATA before anything is launched.  Off by default: the check synchronises.
+bool debug_validate() {
+    const char *e = getenv("KDA_DEBUG_VALIDATE");
+    return e && e[0] == '1' && e[1] == 0;
+}
+
+kda_status debug_check(const int32_t *offsets, int32_t n_off, int64_t total, const int32_t *indices,
+                       int32_t n_idx, int32_t max_slots, void *stream) {
+    if (!debug_validate()) return KDA_OK;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return KDA_ERR_HIP;
+    if (offsets) {
+        const kda_status st = check_offsets(offsets, n_off, total);
+        if (st != KDA_OK) return st;
+    }
+    return indices ? check_indices(indices, n_idx, max_slots) : KDA_OK;
+}
+
 kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, const void *v,
                           const float *raw_gate, const float *beta_logits, const float *a_log,
                           const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
@@ -144,6 +188,9 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
                           size_t workspace_bytes, void *stream) {
     kda_status st = check_fwd(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
                               state_indices, out);
+    if (st != KDA_OK) return st;
+    st = debug_check(cu_seqlens, desc->batch, desc->total_tokens, state_indices, desc->batch, desc->max_slots,
+                     stream);
     if (st != KDA_OK) return st;
     if (desc->batch == 0 || desc->total_tokens == 0) {
         // no tokens: nothing to read or write (every sequence is empty)
@@ -272,6 +319,8 @@ kda_status kda_decode(const kda_desc *desc, const void *q, const void *k, const 
     if (!a_log || !dt_bias || !state_pool || (desc->batch > 0 && !state_indices)) return KDA_ERR_NULL;
     if (desc->batch > 0 && (!q || !k || !v || !raw_gate || !beta_logits || !out)) return KDA_ERR_NULL;
     if (desc->batch == 0) return KDA_OK;
+    const kda_status st = debug_check(nullptr, 0, 0, state_indices, desc->batch, desc->max_slots, stream);
+    if (st != KDA_OK) return st;
     kda::DecodeArgs a;
     memset(&a, 0, sizeof(a));
     a.q = q;
@@ -305,6 +354,8 @@ kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *
     if (n_seg < 1) return KDA_ERR_SHAPE;
     if (!a_log || !dt_bias || !seg_offsets || !M || !U) return KDA_ERR_NULL;
     if (desc->total_tokens > 0 && (!k || !v || !raw_gate || !beta_logits)) return KDA_ERR_NULL;
+    st = debug_check(seg_offsets, n_seg, desc->total_tokens, nullptr, 0, 0, stream);
+    if (st != KDA_OK) return st;
     const bool precise = desc->qkv_dtype == KDA_F32;
     kda::ChainArgs a = base_args(desc);
     a.k = k;
@@ -345,21 +396,8 @@ kda_status kda_validate_varlen(const int32_t *cu_seqlens, int32_t batch, int64_t
                                const int32_t *state_indices, int32_t max_slots) {
     if (batch < 0 || total_tokens < 0 || max_slots <= 0) return KDA_ERR_SHAPE;
     if (!cu_seqlens || (batch > 0 && !state_indices)) return KDA_ERR_NULL;
-    std::vector<int32_t> cu(batch + 1), idx(batch > 0 ? batch : 1);
-    if (hipMemcpy(cu.data(), cu_seqlens, sizeof(int32_t) * (batch + 1), hipMemcpyDeviceToHost) != hipSuccess)
-        return KDA_ERR_HIP;
-    if (batch > 0 &&
-        hipMemcpy(idx.data(), state_indices, sizeof(int32_t) * batch, hipMemcpyDeviceToHost) != hipSuccess)
-        return KDA_ERR_HIP;
-    if (cu[0] != 0 || (int64_t)cu[batch] != total_tokens) return KDA_ERR_DATA;
-    for (int b = 0; b < batch; ++b)
-        if (cu[b + 1] < cu[b]) return KDA_ERR_DATA;
-    std::vector<char> seen(max_slots, 0);
-    for (int b = 0; b < batch; ++b) {
-        if (idx[b] < 0 || idx[b] >= max_slots || seen[idx[b]]) return KDA_ERR_DATA;
-        seen[idx[b]] = 1;
-    }
-    return KDA_OK;
+    const kda_status st = check_offsets(cu_seqlens, batch, total_tokens);
+    return st != KDA_OK ? st : check_indices(state_indices, batch, max_slots);
 }
 
 }  // extern "C"
