@@ -139,11 +139,14 @@ kda_status check_fwd(const kda_desc *desc, const void *q, const void *k, const v
 }
 
 // Host checks of the data-dependent preconditions (synchronous copies to the host).
-kda_status check_offsets(const int32_t *offsets, int32_t n, int64_t total) {
+// exact: offsets start at 0 and end at total (cu_seqlens); else they lie in [0, total]
+// (segment offsets).  Non-decreasing in both cases.
+kda_status check_offsets(const int32_t *offsets, int32_t n, int64_t total, bool exact) {
     std::vector<int32_t> cu(n + 1);
     if (hipMemcpy(cu.data(), offsets, sizeof(int32_t) * (n + 1), hipMemcpyDeviceToHost) != hipSuccess)
         return KDA_ERR_HIP;
-    if (cu[0] != 0 || (int64_t)cu[n] != total) return KDA_ERR_DATA;
+    if (exact ? (cu[0] != 0 || (int64_t)cu[n] != total) : (cu[0] < 0 || (int64_t)cu[n] > total))
+        return KDA_ERR_DATA;
     for (int b = 0; b < n; ++b)
         if (cu[b + 1] < cu[b]) return KDA_ERR_DATA;
     return KDA_OK;
@@ -170,12 +173,12 @@ bool debug_validate() {
     return e && e[0] == '1' && e[1] == 0;
 }
 
-kda_status debug_check(const int32_t *offsets, int32_t n_off, int64_t total, const int32_t *indices,
-                       int32_t n_idx, int32_t max_slots, void *stream) {
+kda_status debug_check(const int32_t *offsets, int32_t n_off, int64_t total, bool exact,
+                       const int32_t *indices, int32_t n_idx, int32_t max_slots, void *stream) {
     if (!debug_validate()) return KDA_OK;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return KDA_ERR_HIP;
     if (offsets) {
-        const kda_status st = check_offsets(offsets, n_off, total);
+        const kda_status st = check_offsets(offsets, n_off, total, exact);
         if (st != KDA_OK) return st;
     }
     return indices ? check_indices(indices, n_idx, max_slots) : KDA_OK;
@@ -189,8 +192,8 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
     kda_status st = check_fwd(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
                               state_indices, out);
     if (st != KDA_OK) return st;
-    st = debug_check(cu_seqlens, desc->batch, desc->total_tokens, state_indices, desc->batch, desc->max_slots,
-                     stream);
+    st = debug_check(cu_seqlens, desc->batch, desc->total_tokens, true, state_indices, desc->batch,
+                     desc->max_slots, stream);
     if (st != KDA_OK) return st;
     if (desc->batch == 0 || desc->total_tokens == 0) {
         // no tokens: nothing to read or write (every sequence is empty)
@@ -319,7 +322,7 @@ kda_status kda_decode(const kda_desc *desc, const void *q, const void *k, const 
     if (!a_log || !dt_bias || !state_pool || (desc->batch > 0 && !state_indices)) return KDA_ERR_NULL;
     if (desc->batch > 0 && (!q || !k || !v || !raw_gate || !beta_logits || !out)) return KDA_ERR_NULL;
     if (desc->batch == 0) return KDA_OK;
-    const kda_status st = debug_check(nullptr, 0, 0, state_indices, desc->batch, desc->max_slots, stream);
+    const kda_status st = debug_check(nullptr, 0, 0, true, state_indices, desc->batch, desc->max_slots, stream);
     if (st != KDA_OK) return st;
     kda::DecodeArgs a;
     memset(&a, 0, sizeof(a));
@@ -354,7 +357,7 @@ kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *
     if (n_seg < 1) return KDA_ERR_SHAPE;
     if (!a_log || !dt_bias || !seg_offsets || !M || !U) return KDA_ERR_NULL;
     if (desc->total_tokens > 0 && (!k || !v || !raw_gate || !beta_logits)) return KDA_ERR_NULL;
-    st = debug_check(seg_offsets, n_seg, desc->total_tokens, nullptr, 0, 0, stream);
+    st = debug_check(seg_offsets, n_seg, desc->total_tokens, false, nullptr, 0, 0, stream);
     if (st != KDA_OK) return st;
     const bool precise = desc->qkv_dtype == KDA_F32;
     kda::ChainArgs a = base_args(desc);
@@ -396,7 +399,7 @@ kda_status kda_validate_varlen(const int32_t *cu_seqlens, int32_t batch, int64_t
                                const int32_t *state_indices, int32_t max_slots) {
     if (batch < 0 || total_tokens < 0 || max_slots <= 0) return KDA_ERR_SHAPE;
     if (!cu_seqlens || (batch > 0 && !state_indices)) return KDA_ERR_NULL;
-    const kda_status st = check_offsets(cu_seqlens, batch, total_tokens);
+    const kda_status st = check_offsets(cu_seqlens, batch, total_tokens, true);
     return st != KDA_OK ? st : check_indices(state_indices, batch, max_slots);
 }
 

@@ -78,3 +78,19 @@ def test_debug_validate_refuses_bad_data(monkeypatch):
     # without the variable, nothing is checked (the call is asynchronous)
     monkeypatch.delenv("KDA_DEBUG_VALIDATE")
     assert os.environ.get("KDA_DEBUG_VALIDATE") is None
+
+
+def test_debug_validate_segment_offsets(monkeypatch):
+    """Segment offsets need only lie in [0, T] and not decrease."""
+    w = wl.custom([300], H=2, dk=128, dv=128, dtype="bf16", gate_mode=1, seed=17)
+    print("[case] KDA_DEBUG_VALIDATE on segment_summary", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+    monkeypatch.setenv("KDA_DEBUG_VALIDATE", "1")
+    args = (inp["k"], inp["v"], inp["raw_gate"], inp["beta_logits"], inp["a_log"], inp["dt_bias"])
+    ok = torch.tensor([10, 100, 290], dtype=torch.int32, device="cuda")   # inside [0, T], not from 0
+    M, U = kda.segment_summary(*args, ok)
+    torch.cuda.synchronize()
+    assert M.shape[0] == 2 and torch.isfinite(M).all() and torch.isfinite(U).all()
+    for bad in ([0, 200, 100], [0, 100, 301], [-1, 100, 200]):
+        with pytest.raises(ValueError):
+            kda.segment_summary(*args, torch.tensor(bad, dtype=torch.int32, device="cuda"))
