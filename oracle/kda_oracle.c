@@ -8,8 +8,9 @@
  *
  * What it computes, and where each step comes from:
  *
- *   Gate (reading; the kda_chunk API page names raw_gate "before dt_bias is
- *   added", a_log and dt_bias, but prints no formula):
+ *   Gate (reading; the kda_chunk API page lists raw_gate as the gate input to
+ *   which dt_bias is still to be added, plus a_log and dt_bias, but gives no
+ *   formula):
  *       x_c  = raw_gate[t,c] + dt_bias[c]
  *       la_c = -exp(a_log) * softplus(x_c),  softplus(x) = max(x,0)+log1p(exp(-|x|))
  *       gate_mode "safe" (kda_chunk API page, gate_mode parameter): la_c = max(la_c, lb)
