@@ -61,7 +61,9 @@ int value_slice(int dk, bool precise) {
     return 64;
 }
 
-bool use_fast(const kda_desc *d) { return d->qkv_dtype == KDA_BF16 && d->dk == 128 && d->dv == 128; }
+bool use_fast(const kda_desc *d) {
+    return d->qkv_dtype == KDA_BF16 && d->dk == d->dv && (d->dk == 128 || d->dk == 64);
+}
 
 constexpr int MAX_DEV = 64;
 
@@ -108,7 +110,10 @@ hipMemPool_t device_pool(int dev) {
     return pools[dev];
 }
 
-bool planned_applies(const kda_desc *d) { return use_fast(d) && d->batch > 0 && d->total_tokens > 0; }
+// The balanced schedule (planner, piece scan, fixup) is built for dk = dv = 128.
+bool planned_applies(const kda_desc *d) {
+    return use_fast(d) && d->dk == 128 && d->batch > 0 && d->total_tokens > 0;
+}
 
 // chunk kernel of the bf16 dk = dv = 128 forward pass
 const kda::FwdKernel &fwd_kernel() { return kda::FWD64; }
@@ -225,7 +230,7 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
             if (workspace_bytes < need) return KDA_ERR_SHAPE;
             e = kda::launch_planned_fwd(a, (char *)workspace, lay, n_cu, fwd_kernel(), (hipStream_t)stream);
         } else {
-            e = kda::launch_fast(a, kda::MODE_FWD, (hipStream_t)stream);
+            e = kda::launch_fast(a, desc->dk, kda::MODE_FWD, (hipStream_t)stream);
         }
     } else {
         const int dvs = value_slice(desc->dk, precise);
@@ -374,7 +379,7 @@ kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *
     hipError_t e;
     if (use_fast(desc)) {
         a.n_slices = 2;
-        e = kda::launch_fast(a, kda::MODE_SUMMARY, (hipStream_t)stream);
+        e = kda::launch_fast(a, desc->dk, kda::MODE_SUMMARY, (hipStream_t)stream);
     } else {
         const int dvs = value_slice(desc->dk, precise);
         a.n_slices = (desc->dk + desc->dv) / dvs;

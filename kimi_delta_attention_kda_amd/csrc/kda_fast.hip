@@ -1,13 +1,13 @@
-// kda_fast.hip -- bf16 chunk-parallel KDA prefill for dk = dv = 128 on gfx950 (MI355X).
+// kda_fast.hip -- bf16 chunk-parallel KDA prefill for dk = dv in {64, 128} on gfx950 (MI355X).
 //
 // Same chunk algebra as the chunk walk in kda_chain.hip (the token recurrence
 // S_t = (I - b k k^T) Diag(alpha) S_{t-1} + b k v^T, o_t = scale q^T S_t of the
 // nx_nofloat_kda.nx source rewritten over 64-token chunks), organised for throughput:
 //
-//  * one workgroup of 8 waves owns one (sequence, head) and all 128 value columns, so
-//    the dv-independent work of a chunk (gate, decay factors, scores, inverses) is done
-//    once; each wave owns one 16-column tile of the fp32 state (128 x 16, in MFMA
-//    accumulators) for the whole sequence;
+//  * one workgroup of dv/16 waves (8 at dv = 128, 4 at dv = 64) owns one (sequence, head)
+//    and all value columns, so the dv-independent work of a chunk (gate, decay factors,
+//    scores, inverses) is done once; each wave owns one 16-column tile of the fp32 state
+//    (dk x 16, in MFMA accumulators) for the whole sequence;
 //  * prep threads own 4 adjacent key channels x 4 rows of one 16-row block: the gate
 //    pre-activations arrive as 16-byte loads, k/q/v as 8-byte loads, operand rows leave
 //    as 8-byte LDS stores; decay factors are running products of alpha (no exp of
@@ -34,14 +34,22 @@ namespace fast {
 
 using namespace fk;
 
-constexpr int NT = 512;  // 8 waves
-constexpr int DK = 128;
-constexpr int DV = 128;
-constexpr int PK = DK + 8;  // 16-bit element pitch of [64][DK] arrays
 constexpr int PJ = 64 + 8;  // 16-bit element pitch of [*][64] arrays
 
-template <int MODE>
+// dk = dv = DKT in {64, 128}: DKT/16 waves, each owning 16 state columns.
+template <int DKT>
+struct Geo {
+    static constexpr int DK = DKT, DV = DKT;
+    static constexpr int NW = DV / 16;      // waves
+    static constexpr int NT = 64 * NW;      // threads
+    static constexpr int NCT = DK / 16;     // 16-row state tiles per wave
+    static constexpr int NKB = DK / 32;     // 32-channel blocks of a score or Kg S product
+    static constexpr int PK = DK + 8;       // 16-bit element pitch of [64][DK] arrays
+};
+
+template <int DKT, int MODE>
 struct Lds {
+    static constexpr int DK = DKT, DV = DKT, PK = Geo<DKT>::PK;
     static constexpr bool FW = MODE == MODE_FWD;
     static constexpr int ROWS = 64 * PK * 2;              // one [64][PK] 16-bit array
     static constexpr int KR = 0;                          // Kr            bf16, scores
@@ -63,21 +71,39 @@ struct Lds {
 };
 
 // Block pairs (I, J <= I) of the 4x4 grid of 16x16 score blocks handled by wave w in the
-// score phase: waves 0-3 take the diagonal pair (w, w); waves 4..7 take the off-diagonal
-// pairs {(1,0),(2,1)}, {(2,0),(3,2)}, {(3,0)}, {(3,1)}.  Arithmetic, so that no memory
-// access (and no wait on the in-flight prefetch) is needed to find them.
-__device__ __forceinline__ int n_pairs_of_wave(int w) { return (w == 4 || w == 5) ? 2 : 1; }
-__device__ __forceinline__ void pair_of_wave(int w, int pp, int &bI, int &bJ) {
-    if (w < 4) { bI = w; bJ = w; return; }
-    if (w == 4) { bI = 1 + pp; bJ = pp; return; }
-    if (w == 5) { bI = 2 + pp; bJ = 2 * pp; return; }
+// score phase.  With 8 waves: waves 0-3 take the diagonal pair (w, w); waves 4..7 take
+// the off-diagonal pairs {(1,0),(2,1)}, {(2,0),(3,2)}, {(3,0)}, {(3,1)}.  With 4 waves,
+// wave w takes (w, w) and then the off-diagonal pairs of wave w + 4.  Arithmetic, so that
+// no memory access (and no wait on the in-flight prefetch) is needed to find them.
+__device__ __forceinline__ int n_offdiag(int v) { return (v == 4 || v == 5) ? 2 : 1; }
+__device__ __forceinline__ void offdiag(int v, int pp, int &bI, int &bJ) {
+    if (v == 4) { bI = 1 + pp; bJ = pp; return; }
+    if (v == 5) { bI = 2 + pp; bJ = 2 * pp; return; }
     bI = 3;
-    bJ = w - 6;
+    bJ = v - 6;
+}
+template <int NW>
+__device__ __forceinline__ int n_pairs_of_wave(int w) {
+    if constexpr (NW == 8) return w < 4 ? 1 : n_offdiag(w);
+    else return 1 + n_offdiag(w + 4);
+}
+template <int NW>
+__device__ __forceinline__ void pair_of_wave(int w, int pp, int &bI, int &bJ) {
+    if constexpr (NW == 8) {
+        if (w < 4) { bI = w; bJ = w; return; }
+        offdiag(w, pp, bI, bJ);
+    } else {
+        if (pp == 0) { bI = w; bJ = w; return; }
+        offdiag(w + 4, pp - 1, bI, bJ);
+    }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
-    using L = Lds<MODE>;
+template <int DKT, int MODE>
+__global__ __launch_bounds__(Geo<DKT>::NT, 512 / Geo<DKT>::NT) void kda_fast_kernel(ChainArgs a) {
+    using L = Lds<DKT, MODE>;
+    using Gm = Geo<DKT>;
+    constexpr int DK = Gm::DK, DV = Gm::DV, NW = Gm::NW, NT = Gm::NT, NCT = Gm::NCT, NKB = Gm::NKB;
+    constexpr int PK = Gm::PK;
     constexpr bool FW = MODE == MODE_FWD;
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     bf16_t *sKR = (bf16_t *)(smem + L::KR);
@@ -100,7 +126,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     const int t = threadIdx.x, l = t & 63, g = l >> 4, li = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, in a scalar register
     // prep role: block I, key channels c0 .. c0+3, rows 16I + 4rq + [0, 4)
-    const int I = __builtin_amdgcn_readfirstlane(t >> 7), rq = t & 3, c0 = 4 * ((t >> 2) & 31);
+    const int I = __builtin_amdgcn_readfirstlane(t / (NT / 4)), rq = t & 3, c0 = 4 * ((t >> 2) & (DK / 4 - 1));
     const int rbase = 16 * I + 4 * rq;
     const float amin = a.gate_mode == 1 ? expf(a.lb) : 0.f;  // alpha floor of the safe gate
     const int xcd = blockIdx.x & 7;  // workgroups are dealt to the 8 XCDs round-robin
@@ -186,11 +212,11 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     // Lane (g, li) holds key rows key_row(ct, 4g + s) = 8g + (32(ct/2) + 4(ct%2) + s) of
     // column 16w + li: one lane pointer per unit plus row offsets times the row stride
     // (DV for [DK][DV] storage, 1 for a V_FIRST slot).
-    f32x4 S[8];
+    f32x4 S[NCT];
     const float *sp = vf ? fin + (16 * w + li) * DK + 8 * g : fin + 8 * g * DV + 16 * w + li;
     const int rstride = vf ? 1 : DV;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int rr = 32 * (ct >> 1) + 4 * (ct & 1) + s;
@@ -389,13 +415,13 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
 
         // ============ P2: decayed scores; diagonal waves also invert their block ============
         {
-            const int np = n_pairs_of_wave(w);
+            const int np = n_pairs_of_wave<NW>(w);
             for (int pp = 0; pp < np; ++pp) {
                 int bI, bJ;
-                pair_of_wave(w, pp, bI, bJ);
+                pair_of_wave<NW>(w, pp, bI, bJ);
                 f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
+                for (int kb = 0; kb < NKB; ++kb) {
                     const int cc = 32 * kb + 8 * g;
                     const bf16x8 aK = *(const bf16x8 *)(sKR + (16 * bI + li) * PK + cc);
                     const bf16x8 kcv = *(const bf16x8 *)(sKC + (16 * bJ + li) * PK + cc);
@@ -462,16 +488,16 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
         f16x4 Uh[4], Ul[4];
         float usc, iusc;  // power-of-two scale of this wave's U and its inverse
         {
-            bf16x8 Sb[4];
+            bf16x8 Sb[NKB];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) Sb[kb] = cat(bf4(S[2 * kb]), bf4(S[2 * kb + 1]));
+            for (int kb = 0; kb < NKB; ++kb) Sb[kb] = cat(bf4(S[2 * kb]), bf4(S[2 * kb + 1]));
             f32x4 Y[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 Y[rt] = zero4();
                 Z[rt] = zero4();
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
+                for (int kb = 0; kb < NKB; ++kb) {
                     Y[rt] = mfma(*(const bf16x8 *)(sKG + (16 * rt + li) * PK + 32 * kb + 8 * g), Sb[kb], Y[rt]);
                     // output transposed, O^T = S^T Qbar^T: the state tile is the A operand
                     if (FW)
@@ -482,9 +508,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             // when the chunk decays it, but accumulates to ~1e-3 of the state where a key
             // channel barely decays.  Chunks in which some channel keeps more than 1/16 of
             // its state over the chunk add the product with the rounding residual of S.
-            if (wave_max_nonneg(fmaxf(sEG[l], sEG[l + 64])) > 0x1p-4f) {
+            if (wave_max_nonneg(DK == 128 ? fmaxf(sEG[l], sEG[l + 64]) : sEG[l]) > 0x1p-4f) {
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
+                for (int kb = 0; kb < NKB; ++kb) {
                     const bf16x8 sh = Sb[kb];
                     const bf16x8 sl = cat(bf4(S[2 * kb] - f4(bf16x4{sh[0], sh[1], sh[2], sh[3]})),
                                           bf4(S[2 * kb + 1] - f4(bf16x4{sh[4], sh[5], sh[6], sh[7]})));
@@ -566,9 +592,9 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             // S <- Diag(e^{G_last}) S + Khat^T U
             if (usc != 1.f)
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct) S[ct] *= usc;
+                for (int ct = 0; ct < NCT; ++ct) S[ct] *= usc;
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
+            for (int ct = 0; ct < NCT; ++ct) {
                 S[ct] *= *(const f32x4 *)(sEG + key_row(ct, 4 * g));
 #pragma unroll
                 for (int jb = 0; jb < 2; ++jb) {
@@ -579,7 +605,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
             }
             if (usc != 1.f)
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct) S[ct] *= iusc;
+                for (int ct = 0; ct < NCT; ++ct) S[ct] *= iusc;
         }
         if (ck + 2 < n_chunks) {
             issue(ck + 2, 0);
@@ -593,7 +619,7 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
     {
         float *fp = vf ? fin + (16 * w + li) * DK + 8 * g : fin + 8 * g * DV + 16 * w + li;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int s = 0; s < 4; ++s) fp[(32 * (ct >> 1) + 4 * (ct & 1) + s) * rstride] = S[ct][s];
     }
@@ -602,20 +628,33 @@ __global__ __launch_bounds__(NT, 1) void kda_fast_kernel(ChainArgs a) {
 
 }  // namespace fast
 
-hipError_t launch_fast(const ChainArgs &a, int mode, hipStream_t stream) {
+namespace {
+template <int DKT>
+void launch_fast_dk(const ChainArgs &a, int mode, dim3 grid, hipStream_t stream) {
+    const dim3 block(fast::Geo<DKT>::NT);
+    if (mode == MODE_FWD)
+        hipLaunchKernelGGL((fast::kda_fast_kernel<DKT, MODE_FWD>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((fast::kda_fast_kernel<DKT, MODE_SUMMARY>), grid, block, 0, stream, a);
+}
+}  // namespace
+
+hipError_t launch_fast(const ChainArgs &a, int dk, int mode, hipStream_t stream) {
     const int n_units = a.n_items * a.H;
     const dim3 grid(8 * a.n_slices * ((n_units + 7) / 8));
-    if (mode == MODE_FWD)
-        hipLaunchKernelGGL(fast::kda_fast_kernel<MODE_FWD>, grid, dim3(fast::NT), 0, stream, a);
+    if (dk == 128)
+        launch_fast_dk<128>(a, mode, grid, stream);
+    else if (dk == 64)
+        launch_fast_dk<64>(a, mode, grid, stream);
     else
-        hipLaunchKernelGGL(fast::kda_fast_kernel<MODE_SUMMARY>, grid, dim3(fast::NT), 0, stream, a);
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t launch_fast_planned(const ChainArgs &a, int n_cu, hipStream_t stream) {
     // persistent: one workgroup per CU (LDS allows no second one), drained queues end it
     const dim3 grid(8 * ((n_cu + 7) / 8));
-    hipLaunchKernelGGL(fast::kda_fast_kernel<MODE_FWD>, grid, dim3(fast::NT), 0, stream, a);
+    launch_fast_dk<128>(a, MODE_FWD, grid, stream);
     return hipGetLastError();
 }
 

@@ -71,10 +71,10 @@ struct ChainArgs {
 // dvs: value columns per workgroup (64 or 128); precise: fp32 inputs.
 hipError_t launch_chain(const ChainArgs &a, int dk, int dvs, bool precise, int mode, hipStream_t stream);
 
-// bf16 inputs, dk = dv = 128, safe gate: 8-wave kernel, one workgroup per (item, head)
+// bf16 inputs, dk = dv in {64, 128}, safe gate: dv/16-wave kernel, one workgroup per (item, head)
 // for the forward pass (n_slices = 1) and two (transition / contribution columns) for
 // segment summaries (n_slices = 2).
-hipError_t launch_fast(const ChainArgs &a, int mode, hipStream_t stream);
+hipError_t launch_fast(const ChainArgs &a, int dk, int mode, hipStream_t stream);
 // forward pass over the queues of a plan (a.plan set), one persistent workgroup per CU
 hipError_t launch_fast_planned(const ChainArgs &a, int n_cu, hipStream_t stream);
 // The chunk kernel of the bf16 dk = dv = 128 forward pass: its chunk length and how many of

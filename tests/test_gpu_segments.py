@@ -102,10 +102,12 @@ def test_segments_against_serial_replay(name):
         _assert_close(wl.as_f64(U[i, h]), U_ref, STATE_TOL, f"U seg={i} h={h}")
 
 
-def test_bf16_segment_summary_small():
+@pytest.mark.parametrize("dk", [128, 64])
+def test_bf16_segment_summary_small(dk):
     from kda_testlib import STATE_TOL
-    w = wl.Workload("bf16_segments", (3 * 700,), 2, 128, 128, "bf16", 1, n_slots=1, state_sigma=0.01,
+    w = wl.Workload("bf16_segments", (3 * 700,), 2, dk, dk, "bf16", 1, n_slots=1, state_sigma=0.01,
                     segments=3, seed=4, raw_mean=-6.0, a_log_hi=0.0, beta_mean=-4.0)
+    print(f"[case] bf16 segment summaries dk={dk}", flush=True)
     inp = wl.make_inputs(w, "cuda")
     M, U, inc, outg, fin = _summaries(w, inp)
     pairs = [(i, h) for i in range(3) for h in range(2)]
