@@ -69,14 +69,14 @@ typedef enum { KDA_STATE_K_FIRST = 0, KDA_STATE_V_FIRST = 1 } kda_state_layout;
  * Shapes and modes of one call (max.nn.state_space.kda_chunk, Parameters).
  * num_heads is both the key-head and value-head count (equal counts, as in the
  * gfx950 contract of kda_chunk).
- * Supported contract (anything else -> KDA_ERR_UNSUPPORTED):
- *   qkv_dtype == out_dtype;
- *   bf16: dk == dv in {64, 128}, gate_mode SAFE with -5.3 <= gate_lower_bound <= 0
- *         (the 16-token factorisation of the decay needs 16*|bound| < 85);
- *   f32:  dk == dv == 64 for kda_chunk_fwd; dk == dv in {64, 128} for
- *         kda_segment_summary; either gate mode;
- *   kda_decode: dk == dv in {64, 128}, bf16 or f32, either gate mode;
+ * Supported contract (anything else -> KDA_ERR_UNSUPPORTED), for kda_chunk_fwd,
+ * kda_segment_summary and kda_decode alike:
+ *   qkv_dtype == out_dtype, bf16 or f32; dk == dv in {64, 128}; either gate mode;
  *   state_layout K_FIRST ([slot][H][dk][dv]) or V_FIRST ([slot][H][dv][dk]).
+ * Speed differs by range: bf16 with the SAFE gate and gate_lower_bound >= -5.3 runs
+ * the fast chunk kernel (the gfx950 contract of kda_chunk: bf16, safe gate; its
+ * 16-token factorisation of the decay needs 16*|bound| < 85); other calls run a
+ * slower chunk walk that evaluates every decay factor directly, at fp32 accuracy.
  */
 typedef struct {
     int64_t total_tokens;    /* T: rows of q, k, v, raw_gate, beta_logits, out   */

@@ -28,17 +28,7 @@ kda_status check_desc(const kda_desc *d, bool summary) {
     // ---- supported contract
     if (d->dk != d->dv) return KDA_ERR_UNSUPPORTED;
     if (!summary && d->qkv_dtype != d->out_dtype) return KDA_ERR_UNSUPPORTED;
-    if (d->qkv_dtype == KDA_BF16) {
-        if (d->dk != 64 && d->dk != 128) return KDA_ERR_UNSUPPORTED;
-        if (d->gate_mode != KDA_GATE_SAFE) return KDA_ERR_UNSUPPORTED;
-        if (d->gate_lower_bound < -5.3f) return KDA_ERR_UNSUPPORTED;
-    } else {
-        if (summary) {
-            if (d->dk != 64 && d->dk != 128) return KDA_ERR_UNSUPPORTED;
-        } else {
-            if (d->dk != 64) return KDA_ERR_UNSUPPORTED;
-        }
-    }
+    if (d->dk != 64 && d->dk != 128) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
 }
 
@@ -54,15 +44,15 @@ kda::ChainArgs base_args(const kda_desc *d) {
     return a;
 }
 
-// Value columns per workgroup of the general chunk walk (kda_chain.hip).
-int value_slice(int dk, bool precise) {
-    (void)dk;
-    (void)precise;
-    return 64;
-}
+// Value columns per workgroup of the precise chunk walk (kda_chain.hip).
+constexpr int CHAIN_SLICE = 64;
 
+// The fast kernel (kda_fast.hip) takes bf16 with the safe gate, whose bound keeps the
+// reciprocal of a 16-token block decay, e^{16 |bound|}, finite; everything else within
+// the contract runs the precise chunk walk.
 bool use_fast(const kda_desc *d) {
-    return d->qkv_dtype == KDA_BF16 && d->dk == d->dv && (d->dk == 128 || d->dk == 64);
+    return d->qkv_dtype == KDA_BF16 && d->dk == d->dv && (d->dk == 128 || d->dk == 64) &&
+           d->gate_mode == KDA_GATE_SAFE && d->gate_lower_bound >= -5.3f;
 }
 
 constexpr int MAX_DEV = 64;
@@ -204,7 +194,6 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
         // no tokens: nothing to read or write (every sequence is empty)
         return KDA_OK;
     }
-    const bool precise = desc->qkv_dtype == KDA_F32;
     kda::ChainArgs a = base_args(desc);
     a.q = q;
     a.k = k;
@@ -233,9 +222,8 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
             e = kda::launch_fast(a, desc->dk, kda::MODE_FWD, (hipStream_t)stream);
         }
     } else {
-        const int dvs = value_slice(desc->dk, precise);
-        a.n_slices = desc->dv / dvs;
-        e = kda::launch_chain(a, desc->dk, dvs, precise, kda::MODE_FWD, (hipStream_t)stream);
+        a.n_slices = desc->dv / CHAIN_SLICE;
+        e = kda::launch_chain(a, desc->dk, desc->qkv_dtype == KDA_BF16, kda::MODE_FWD, (hipStream_t)stream);
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -364,7 +352,6 @@ kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *
     if (desc->total_tokens > 0 && (!k || !v || !raw_gate || !beta_logits)) return KDA_ERR_NULL;
     st = debug_check(seg_offsets, n_seg, desc->total_tokens, false, nullptr, 0, 0, stream);
     if (st != KDA_OK) return st;
-    const bool precise = desc->qkv_dtype == KDA_F32;
     kda::ChainArgs a = base_args(desc);
     a.k = k;
     a.v = v;
@@ -381,9 +368,8 @@ kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *
         a.n_slices = 2;
         e = kda::launch_fast(a, desc->dk, kda::MODE_SUMMARY, (hipStream_t)stream);
     } else {
-        const int dvs = value_slice(desc->dk, precise);
-        a.n_slices = (desc->dk + desc->dv) / dvs;
-        e = kda::launch_chain(a, desc->dk, dvs, precise, kda::MODE_SUMMARY, (hipStream_t)stream);
+        a.n_slices = (desc->dk + desc->dv) / CHAIN_SLICE;
+        e = kda::launch_chain(a, desc->dk, desc->qkv_dtype == KDA_BF16, kda::MODE_SUMMARY, (hipStream_t)stream);
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -1,8 +1,19 @@
 // kda_fast.hip -- bf16 chunk-parallel KDA prefill for dk = dv in {64, 128} on gfx950 (MI355X).
 //
-// Same chunk algebra as the chunk walk in kda_chain.hip (the token recurrence
+// Same chunk algebra as the precise walk in kda_chain.hip (the token recurrence
 // S_t = (I - b k k^T) Diag(alpha) S_{t-1} + b k v^T, o_t = scale q^T S_t of the
-// nx_nofloat_kda.nx source rewritten over 64-token chunks), organised for throughput:
+// nx_nofloat_kda.nx source rewritten over 64-token chunks), organised for throughput.
+//
+// Stable exponent differences.  Products e^{G_i - G_j} (j <= i, G the running sum of
+// log alpha) never form e^{-G}: the chunk is cut into four 16-row blocks; row i of block
+// I is scaled by e^{G_i - G_(16I-1)} <= 1, row j of block J by e^{G_(16J+15) - G_j} <= 1,
+// and the remaining per-channel factor e^{G_(16I-1) - G_(16J+15)} is a product of
+// whole-block decays (<= 1) for J < I, or the reciprocal of block I's decay for J = I.
+// That reciprocal is <= e^{16 |bound|}, finite in fp32 and bf16 while 16 |bound| < 85:
+// the reason this kernel takes the safe gate only (max.nn.state_space.kda_chunk: the
+// gfx950 pipeline requires gate_mode "safe").  Every factor is a running product of
+// alpha, so the gate's own three transcendentals are the only ones per element.
+//
 //
 //  * one workgroup of dv/16 waves (8 at dv = 128, 4 at dv = 64) owns one (sequence, head)
 //    and all value columns, so the dv-independent work of a chunk (gate, decay factors,
@@ -13,7 +24,7 @@
 //    as 8-byte LDS stores; decay factors are running products of alpha (no exp of
 //    differences), completed across the four quarter blocks with quad lane broadcasts;
 //  * decayed scores come from bf16 MFMAs on 16x16 blocks whose operands carry factors
-//    <= 1, times one per-channel factor per block pair (see kda_chain.hip);
+//    <= 1, times one per-channel factor per block pair (above);
 //  * (I + A) U = R is solved per wave by blocked forward substitution with fp16
 //    16x16x16 MFMAs: 16x16 diagonal-block inverses (fp32 right-looking substitution,
 //    once per chunk) and the right-hand side split into fp16 hi + lo;

@@ -68,8 +68,10 @@ struct ChainArgs {
     void *ws_W;              // [T][H][dv] bf16, W rows of the later pieces
 };
 
-// dvs: value columns per workgroup (64 or 128); precise: fp32 inputs.
-hipError_t launch_chain(const ChainArgs &a, int dk, int dvs, bool precise, int mode, hipStream_t stream);
+// Precise chunk walk (kda_chain.hip): dk = dv in {64, 128}, 64 value columns per
+// workgroup (a.n_slices = dv / 64 for the forward pass, (dk + dv) / 64 for summaries);
+// bf16_in: q/k/v (and out) are bf16, else fp32.
+hipError_t launch_chain(const ChainArgs &a, int dk, bool bf16_in, int mode, hipStream_t stream);
 
 // bf16 inputs, dk = dv in {64, 128}, safe gate: dv/16-wave kernel, one workgroup per (item, head)
 // for the forward pass (n_slices = 1) and two (transition / contribution columns) for

@@ -102,12 +102,13 @@ def test_segments_against_serial_replay(name):
         _assert_close(wl.as_f64(U[i, h]), U_ref, STATE_TOL, f"U seg={i} h={h}")
 
 
-@pytest.mark.parametrize("dk", [128, 64])
-def test_bf16_segment_summary_small(dk):
+@pytest.mark.parametrize("dk,gate", [(128, 1), (64, 1), (128, 0)])
+def test_bf16_segment_summary_small(dk, gate):
+    """bf16 summaries: the fast kernel with the safe gate, the precise walk with the original."""
     from kda_testlib import STATE_TOL
-    w = wl.Workload("bf16_segments", (3 * 700,), 2, dk, dk, "bf16", 1, n_slots=1, state_sigma=0.01,
+    w = wl.Workload("bf16_segments", (3 * 700,), 2, dk, dk, "bf16", gate, n_slots=1, state_sigma=0.01,
                     segments=3, seed=4, raw_mean=-6.0, a_log_hi=0.0, beta_mean=-4.0)
-    print(f"[case] bf16 segment summaries dk={dk}", flush=True)
+    print(f"[case] bf16 segment summaries dk={dk} gate_mode={gate}", flush=True)
     inp = wl.make_inputs(w, "cuda")
     M, U, inc, outg, fin = _summaries(w, inp)
     pairs = [(i, h) for i in range(3) for h in range(2)]

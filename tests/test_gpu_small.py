@@ -61,3 +61,23 @@ def test_fp32_ragged_safe_and_original():
         eo, es = compare_items(w, inp, out, pool, _all_items(w))
         print(f"  out_err={eo:.3e} state_err={es:.3e}", flush=True)
         assert eo <= OUT_TOL_F32 and es <= STATE_TOL
+
+
+@pytest.mark.parametrize("dtype,dk,gate,lb", [("f32", 128, 0, -5.0), ("f32", 128, 1, -5.0),
+                                               ("bf16", 64, 0, -5.0), ("bf16", 128, 0, -5.0),
+                                               ("bf16", 128, 1, -8.0)])
+def test_precise_walk_ragged(dtype, dk, gate, lb):
+    """Calls outside the fast kernel's range -- fp32 inputs, or bf16 with the original gate
+    (decays down to about e^-48 per token here) or a safe bound below -5.3 -- run the
+    precise chunk walk; ragged lengths around the chunk size, an empty sequence."""
+    from kda_testlib import compare_items, run_fwd, untouched_slots_identical
+    from kda_testlib import OUT_TOL_BF16, OUT_TOL_F32, STATE_TOL
+    w = wl.custom([65, 1, 0, 130, 64], H=2, dk=dk, dv=dk, dtype=dtype, gate_mode=gate, seed=21,
+                  lower_bound=lb)
+    print(f"[case] precise walk {dtype} dk={dk} gate_mode={gate} bound={lb}", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+    out, pool = run_fwd(w, inp)
+    eo, es = compare_items(w, inp, out, pool, _all_items(w))
+    print(f"  out_err={eo:.3e} state_err={es:.3e}", flush=True)
+    assert eo <= (OUT_TOL_BF16 if dtype == "bf16" else OUT_TOL_F32) and es <= STATE_TOL
+    assert untouched_slots_identical(inp, pool)

@@ -76,13 +76,13 @@ def test_chunk_fwd_error_paths(L):
     assert _fwd(L, _desc(H=0)) == ESHAPE
     assert _fwd(L, _desc(max_slots=0)) == ESHAPE
     assert _fwd(L, _desc(qkv_dtype=torch.float16)) == EDTYPE
-    assert _fwd(L, _desc(gate_mode="original")) == EUNSUP          # bf16 needs the safe gate
-    assert _fwd(L, _desc(lower_bound=-6.0)) == EUNSUP               # 16*|bound| must stay < 85
     assert _fwd(L, _desc(lower_bound=0.5)) == EARG
     assert _fwd(L, _desc(dk=128, dv=64)) == EUNSUP
     assert _fwd(L, _desc(dk=96, dv=96)) == EUNSUP
+    assert _fwd(L, _desc(dk=32, dv=32, qkv_dtype=torch.float32, out_dtype=torch.float32)) == EUNSUP
     assert _fwd(L, _desc(out_dtype=torch.float32)) == EUNSUP
-    assert _fwd(L, _desc(qkv_dtype=torch.float32, out_dtype=torch.float32)) == EUNSUP  # f32 fwd: dk 64
+    # either gate, any bound <= 0, bf16 or f32 at dk = dv in {64, 128} are in the contract
+    # (launching them needs a GPU, so they are exercised by the GPU tests)
     d = _desc(dk=96, dv=96)
     d.state_layout = 1                                              # V_FIRST is in the contract;
     assert _fwd(L, d) == EUNSUP                                     # dk 96 is not
@@ -114,7 +114,7 @@ def test_workspace_variant_error_paths(L):
     assert _fwd_ws(L, None) == ENULL
     assert _fwd_ws(L, _desc(), out=None) == ENULL
     assert _fwd_ws(L, _desc(T=-1)) == ESHAPE
-    assert _fwd_ws(L, _desc(gate_mode="original")) == EUNSUP
+    assert _fwd_ws(L, _desc(dk=96, dv=96)) == EUNSUP
     assert _fwd_ws(L, _desc(B=0)) == OK
     n = C.c_size_t(7)
     assert L.kda_chunk_fwd_workspace_size(None, C.byref(n)) == ENULL
@@ -124,6 +124,9 @@ def test_workspace_variant_error_paths(L):
                                                          dk=64, dv=64)), C.byref(n)) == OK
     assert n.value == 0
     assert L.kda_chunk_fwd_workspace_size(C.byref(_desc(dk=64, dv=64)), C.byref(n)) == OK
+    assert n.value == 0
+    # neither does the precise walk (bf16 with the original gate)
+    assert L.kda_chunk_fwd_workspace_size(C.byref(_desc(gate_mode="original")), C.byref(n)) == OK
     assert n.value == 0
     # bf16 dk = dv = 128 sizes for the current device (HIP error without one)
     st = L.kda_chunk_fwd_workspace_size(C.byref(_desc()), C.byref(n))
