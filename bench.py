@@ -58,9 +58,11 @@ def algorithmic_bytes(w) -> int:
     """Compulsory HBM bytes of one call: every input read once, out written once,
     each used pool slot read and written once."""
     e_qkv = 2 if w.dtype == "bf16" else 4
-    per_token_head = 2 * w.dk * e_qkv + w.dv * e_qkv + w.dv * e_qkv + w.dk * 4 + 4
+    # per value head: v, out, gate pre-activations, beta; q and k over the key heads
+    per_token_head = w.dv * e_qkv + w.dv * e_qkv + w.dk * 4 + 4
     pool = 2 * w.B * w.H * w.dk * w.dv * 4
-    return w.T * w.H * per_token_head + pool + w.H * (w.dk + 1) * 4 + (w.B + 1) * 4 + w.B * 4
+    return (w.T * (w.H * per_token_head + w.HK * 2 * w.dk * e_qkv) + pool + w.H * (w.dk + 1) * 4
+            + (w.B + 1) * 4 + w.B * 4)
 
 
 def algorithmic_flops(w) -> int:
@@ -77,8 +79,8 @@ def decode_bytes(w) -> int:
     fp32 state once and reads one token's q, k, v, gate pre-activations and beta logit,
     writing one output row."""
     e = 2 if w.dtype == "bf16" else 4
-    per_seq_head = 2 * w.dk * w.dv * 4 + (2 * w.dk + w.dv) * e + w.dv * e + w.dk * 4 + 4
-    return w.B * w.H * per_seq_head + w.H * (w.dk + 1) * 4 + w.B * 4
+    per_seq_head = 2 * w.dk * w.dv * 4 + w.dv * e + w.dv * e + w.dk * 4 + 4
+    return w.B * (w.H * per_seq_head + w.HK * 2 * w.dk * e) + w.H * (w.dk + 1) * 4 + w.B * 4
 
 
 def cpu_baseline(w, inp, target_s=12.0):

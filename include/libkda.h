@@ -67,8 +67,12 @@ typedef enum { KDA_STATE_K_FIRST = 0, KDA_STATE_V_FIRST = 1 } kda_state_layout;
 
 /*
  * Shapes and modes of one call (max.nn.state_space.kda_chunk, Parameters).
- * num_heads is both the key-head and value-head count (equal counts, as in the
- * gfx950 contract of kda_chunk).
+ * num_heads is the value-head count H: of v, the gates, beta, the state pool
+ * and out.  q and k have num_key_heads heads Hk (kda_chunk, Parameters: q and
+ * k are laid out over the key heads, everything else over the value heads).
+ * Hk must divide H; value head h reads key head h / (H / Hk), so each key head
+ * serves H / Hk consecutive value heads.  0 means Hk = H, the gfx950 contract
+ * of kda_chunk.
  * Supported contract (anything else -> KDA_ERR_UNSUPPORTED), for kda_chunk_fwd,
  * kda_segment_summary and kda_decode alike:
  *   qkv_dtype == out_dtype, bf16 or f32; dk == dv in {64, 128}; either gate mode;
@@ -92,11 +96,12 @@ typedef struct {
     int32_t beta_mode;       /* kda_beta_mode                                    */
     int32_t state_layout;    /* kda_state_layout                                 */
     float scale;             /* o = scale * q^T S (callers usually pass 1/sqrt(dk)) */
+    int32_t num_key_heads;   /* Hk: heads of q and k, dividing num_heads; 0 = H  */
 } kda_desc;
 
 /*
  * Chunk-parallel varlen prefill (max.nn.state_space.kda_chunk).
- *   q, k        [T, H, dk]   qkv_dtype
+ *   q, k        [T, Hk, dk]  qkv_dtype
  *   v           [T, H, dv]   qkv_dtype
  *   raw_gate    [T, H, dk]   f32, forget-gate pre-activation before dt_bias
  *   beta_logits [T, H]       f32
@@ -154,7 +159,7 @@ kda_status kda_chunk_fwd_workspace_size(const kda_desc *desc, size_t *bytes);
  * of the nx_nofloat_kda.nx source's kda_step (decay, delta-write, read):
  *   S <- Diag(alpha) S;  S <- S + k (beta (v - S^T k))^T;  o = scale * S^T q,
  * on the pool slot state_indices[b] of each sequence b, in fp32.
- *   q, k [B, H, dk], v [B, H, dv] (qkv_dtype); raw_gate [B, H, dk] f32;
+ *   q, k [B, Hk, dk], v [B, H, dv] (qkv_dtype); raw_gate [B, H, dk] f32;
  *   beta_logits [B, H] f32; a_log [H]; dt_bias [H, dk]; state_pool as for
  *   kda_chunk_fwd (per desc->state_layout); state_indices [B] distinct;
  *   out [B, H, dv] (out_dtype).  desc->total_tokens must equal desc->batch.
@@ -172,7 +177,7 @@ kda_status kda_decode(const kda_desc *desc, const void *q, const void *k, const 
  * covers tokens [seg_offsets[i], seg_offsets[i+1]) of one sequence; for each
  * head, U_i is the segment's state when started from S = 0 and M_i the
  * product, later tokens on the left, of (I - beta k k^T) Diag(alpha).
- *   k [T, H, dk], v [T, H, dv] (qkv_dtype); raw_gate, beta_logits, a_log,
+ *   k [T, Hk, dk], v [T, H, dv] (qkv_dtype); raw_gate, beta_logits, a_log,
  *   dt_bias as for kda_chunk_fwd; seg_offsets [n_seg+1] int32 (device),
  *   monotone with seg_offsets[0] >= 0 and seg_offsets[n_seg] <= T;
  *   M [n_seg, H, dk, dk] f32, U [n_seg, H, dk, dv] f32 (written).

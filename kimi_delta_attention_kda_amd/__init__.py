@@ -35,7 +35,7 @@ class KdaDesc(C.Structure):
                 ("dk", C.c_int32), ("dv", C.c_int32), ("max_slots", C.c_int32),
                 ("qkv_dtype", C.c_int32), ("out_dtype", C.c_int32), ("gate_mode", C.c_int32),
                 ("gate_lower_bound", C.c_float), ("beta_mode", C.c_int32),
-                ("state_layout", C.c_int32), ("scale", C.c_float)]
+                ("state_layout", C.c_int32), ("scale", C.c_float), ("num_key_heads", C.c_int32)]
 
 
 _lib = None
@@ -95,13 +95,22 @@ def _need(t, name, dtype=None, device=None):
 
 
 def make_desc(T, B, H, dk, dv, max_slots, qkv_dtype, out_dtype, gate_mode="safe", lower_bound=-5.0,
-              beta_mode="logits", state_layout="K_FIRST", scale=None) -> KdaDesc:
+              beta_mode="logits", state_layout="K_FIRST", scale=None, Hk=None) -> KdaDesc:
+    """Hk: key heads of q and k (None: as many as the value heads H)."""
     if gate_mode not in _GATE or beta_mode not in _BETA or state_layout not in _LAYOUT:
         raise ValueError("unknown gate_mode / beta_mode / state_layout")
     return KdaDesc(int(T), int(B), int(H), int(dk), int(dv), int(max_slots),
                    _DT.get(qkv_dtype, -1), _DT.get(out_dtype, -1), _GATE[gate_mode],
                    float(lower_bound), _BETA[beta_mode], _LAYOUT[state_layout],
-                   float(1.0 / math.sqrt(dk) if scale is None else scale))
+                   float(1.0 / math.sqrt(dk) if scale is None else scale), int(H if Hk is None else Hk))
+
+
+def _heads(q_or_k, v):
+    """(H, Hk): value heads from v, key heads from q/k; Hk must divide H."""
+    H, Hk = v.shape[1], q_or_k.shape[1]
+    if Hk <= 0 or H % Hk != 0:
+        raise ValueError("the key heads of q and k must divide the value heads of v")
+    return H, Hk
 
 
 def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool, state_indices,
@@ -109,10 +118,11 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
               state_layout="K_FIRST", scale=None, out=None, workspace="torch"):
     """Chunk-parallel varlen KDA prefill; mutates state_pool[state_indices] in place.
 
-    Shapes follow max.nn.state_space.kda_chunk: q,k [T,H,dk]; v [T,H,dv]; raw_gate
+    Shapes follow max.nn.state_space.kda_chunk: q,k [T,Hk,dk]; v [T,H,dv]; raw_gate
     [T,H,dk] f32; beta_logits [T,H] f32; a_log [H] f32; dt_bias [H,dk] f32; cu_seqlens
     [B+1] int32; state_pool [slots,H,dk,dv] f32; state_indices [B] int32.  Returns out
-    [T,H,dv] in output_dtype (default: q's dtype).
+    [T,H,dv] in output_dtype (default: q's dtype).  Hk (key heads) divides H (value
+    heads); value head h reads key head h // (H // Hk).
 
     workspace: "torch" (load-balanced pass, workspace from torch's allocator on the
     current stream), "library" (kda_chunk_fwd: the library's own stream-ordered pool) or
@@ -120,7 +130,10 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
     """
     if workspace not in ("torch", "library", "none"):
         raise ValueError("workspace must be 'torch', 'library' or 'none'")
-    T, H, dk = q.shape
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("ranks and extents of the inputs disagree")
+    T, _, dk = q.shape
+    H, Hk = _heads(q, v)
     dv = v.shape[-1]
     dev = q.device
     B = cu_seqlens.numel() - 1
@@ -132,7 +145,7 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
     _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
     _need(state_indices, "state_indices", torch.int32, dev)
     slot_shape = (H, dk, dv) if state_layout == "K_FIRST" else (H, dv, dk)
-    if k.shape != (T, H, dk) or v.shape[:2] != (T, H) or raw_gate.shape != (T, H, dk) \
+    if k.shape != (T, Hk, dk) or v.shape[:2] != (T, H) or raw_gate.shape != (T, H, dk) \
             or beta_logits.shape != (T, H) or a_log.shape != (H,) or dt_bias.shape != (H, dk) \
             or state_pool.dim() != 4 or state_pool.shape[1:] != slot_shape \
             or state_indices.shape != (B,):
@@ -143,7 +156,7 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
     else:
         _need(out, "out", odt, dev)
     d = make_desc(T, B, H, dk, dv, state_pool.shape[0], q.dtype, odt, gate_mode, lower_bound,
-                  beta_mode, state_layout, scale)
+                  beta_mode, state_layout, scale, Hk)
     args = (C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(beta_logits), _ptr(a_log),
             _ptr(dt_bias), _ptr(cu_seqlens), _ptr(state_pool), _ptr(state_indices), _ptr(out))
     if workspace == "library":
@@ -165,11 +178,14 @@ def decode(q, k, v, raw_gate, beta_logits, a_log, dt_bias, state_pool, state_ind
            state_layout="K_FIRST", scale=None, out=None):
     """One recurrent step per sequence on its pool slot (single-token decode).
 
-    q, k [B,H,dk]; v [B,H,dv]; raw_gate [B,H,dk] f32; beta_logits [B,H] f32; a_log [H];
+    q, k [B,Hk,dk]; v [B,H,dv]; raw_gate [B,H,dk] f32; beta_logits [B,H] f32; a_log [H];
     dt_bias [H,dk]; state_pool [slots,H,dk,dv] (V_FIRST: [slots,H,dv,dk]) f32, mutated at
     state_indices [B] int32.  Returns out [B,H,dv] in output_dtype (default: q's dtype).
     """
-    B, H, dk = q.shape
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("ranks and extents of the inputs disagree")
+    B, _, dk = q.shape
+    H, Hk = _heads(q, v)
     dv = v.shape[-1]
     dev = q.device
     for t_, n_ in ((q, "q"), (k, "k"), (v, "v")):
@@ -179,7 +195,7 @@ def decode(q, k, v, raw_gate, beta_logits, a_log, dt_bias, state_pool, state_ind
         _need(t_, n_, torch.float32, dev)
     _need(state_indices, "state_indices", torch.int32, dev)
     slot_shape = (H, dk, dv) if state_layout == "K_FIRST" else (H, dv, dk)
-    if k.shape != (B, H, dk) or v.shape[:2] != (B, H) or raw_gate.shape != (B, H, dk) \
+    if k.shape != (B, Hk, dk) or v.shape[:2] != (B, H) or raw_gate.shape != (B, H, dk) \
             or beta_logits.shape != (B, H) or a_log.shape != (H,) or dt_bias.shape != (H, dk) \
             or state_pool.dim() != 4 or state_pool.shape[1:] != slot_shape or state_indices.shape != (B,):
         raise ValueError("ranks and extents of the inputs disagree")
@@ -189,7 +205,7 @@ def decode(q, k, v, raw_gate, beta_logits, a_log, dt_bias, state_pool, state_ind
     else:
         _need(out, "out", odt, dev)
     d = make_desc(B, B, H, dk, dv, state_pool.shape[0], q.dtype, odt, gate_mode, lower_bound,
-                  beta_mode, state_layout, scale)
+                  beta_mode, state_layout, scale, Hk)
     _check(lib().kda_decode(C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(beta_logits),
                             _ptr(a_log), _ptr(dt_bias), _ptr(state_pool), _ptr(state_indices), _ptr(out),
                             _stream()))
@@ -200,8 +216,12 @@ def segment_summary(k, v, raw_gate, beta_logits, a_log, dt_bias, seg_offsets, *,
                     lower_bound=-5.0, beta_mode="logits", M=None, U=None):
     """Affine map F_i(S) = M_i S + U_i of every segment [seg_offsets[i], seg_offsets[i+1]).
 
-    Returns M [n_seg,H,dk,dk] f32 and U [n_seg,H,dk,dv] f32."""
-    T, H, dk = k.shape
+    k [T,Hk,dk] and v [T,H,dv] (bf16 or f32); raw_gate [T,H,dk], beta_logits [T,H], a_log [H],
+    dt_bias [H,dk] f32.  Returns M [n_seg,H,dk,dk] f32 and U [n_seg,H,dk,dv] f32."""
+    if k.dim() != 3 or v.dim() != 3:
+        raise ValueError("ranks and extents of the inputs disagree")
+    T, _, dk = k.shape
+    H, Hk = _heads(k, v)
     dv = v.shape[-1]
     dev = k.device
     n_seg = seg_offsets.numel() - 1
@@ -211,11 +231,14 @@ def segment_summary(k, v, raw_gate, beta_logits, a_log, dt_bias, seg_offsets, *,
                    (dt_bias, "dt_bias")):
         _need(t_, n_, torch.float32, dev)
     _need(seg_offsets, "seg_offsets", torch.int32, dev)
+    if v.shape[0] != T or raw_gate.shape != (T, H, dk) or beta_logits.shape != (T, H) \
+            or a_log.shape != (H,) or dt_bias.shape != (H, dk):
+        raise ValueError("ranks and extents of the inputs disagree")
     if M is None:
         M = torch.empty((max(n_seg, 0), H, dk, dk), dtype=torch.float32, device=dev)
     if U is None:
         U = torch.empty((max(n_seg, 0), H, dk, dv), dtype=torch.float32, device=dev)
-    d = make_desc(T, 1, H, dk, dv, 1, k.dtype, k.dtype, gate_mode, lower_bound, beta_mode)
+    d = make_desc(T, 1, H, dk, dv, 1, k.dtype, k.dtype, gate_mode, lower_bound, beta_mode, Hk=Hk)
     _check(lib().kda_segment_summary(C.byref(d), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(beta_logits),
                                      _ptr(a_log), _ptr(dt_bias), _ptr(seg_offsets), int(n_seg),
                                      _ptr(M), _ptr(U), _stream()))

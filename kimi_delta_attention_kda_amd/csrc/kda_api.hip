@@ -13,10 +13,17 @@ namespace {
 
 bool valid_dtype(int32_t d) { return d == KDA_F32 || d == KDA_BF16; }
 
+// Key heads of q and k (0 in the descriptor: as many as value heads).
+int key_heads(const kda_desc *d) { return d->num_key_heads == 0 ? d->num_heads : d->num_key_heads; }
+bool key_heads_ok(const kda_desc *d) {
+    return d->num_key_heads >= 0 && d->num_heads % key_heads(d) == 0;
+}
+
 // Common host-visible checks of the descriptor for the chunk walk.
 kda_status check_desc(const kda_desc *d, bool summary) {
     if (!d) return KDA_ERR_NULL;
     if (d->total_tokens < 0 || d->num_heads <= 0 || d->dk <= 0 || d->dv <= 0) return KDA_ERR_SHAPE;
+    if (!key_heads_ok(d)) return KDA_ERR_SHAPE;
     if (d->total_tokens > (int64_t)0x7fffffff) return KDA_ERR_SHAPE;  // int32 offsets
     if (!summary && (d->batch < 0 || d->max_slots <= 0)) return KDA_ERR_SHAPE;
     if (!valid_dtype(d->qkv_dtype) || (!summary && !valid_dtype(d->out_dtype))) return KDA_ERR_DTYPE;
@@ -36,6 +43,7 @@ kda::ChainArgs base_args(const kda_desc *d) {
     kda::ChainArgs a;
     memset(&a, 0, sizeof(a));
     a.H = d->num_heads;
+    a.Hk = key_heads(d);
     a.gate_mode = d->gate_mode;
     a.lb = d->gate_lower_bound;
     a.beta_mode = d->beta_mode;
@@ -303,6 +311,7 @@ kda_status kda_decode(const kda_desc *desc, const void *q, const void *k, const 
     const kda_desc *d = desc;
     if (!d) return KDA_ERR_NULL;
     if (d->batch < 0 || d->num_heads <= 0 || d->dk <= 0 || d->dv <= 0 || d->max_slots <= 0) return KDA_ERR_SHAPE;
+    if (!key_heads_ok(d)) return KDA_ERR_SHAPE;
     if (d->total_tokens != d->batch) return KDA_ERR_SHAPE;  // one token per sequence
     if (!valid_dtype(d->qkv_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_DTYPE;
     if (d->gate_mode != KDA_GATE_ORIGINAL && d->gate_mode != KDA_GATE_SAFE) return KDA_ERR_ARG;
@@ -331,6 +340,7 @@ kda_status kda_decode(const kda_desc *desc, const void *q, const void *k, const 
     a.out = out;
     a.B = desc->batch;
     a.H = desc->num_heads;
+    a.Hk = key_heads(desc);
     a.gate_mode = desc->gate_mode;
     a.lb = desc->gate_lower_bound;
     a.beta_mode = desc->beta_mode;

@@ -178,6 +178,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
     const int unit = (jx / a.n_slices) * 8 + xcd;
     if (unit >= n_units) return;
     const int item = unit / H, h = unit - item * H;
+    const int hk = h / (H / a.Hk);  // key head of value head h
     const int t_begin = a.offsets[item], t_end = a.offsets[item + 1];
     const int len = t_end - t_begin;
     if (FW && len <= 0) return;  // empty sequence: slot untouched, no rows
@@ -245,10 +246,12 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int i = i0 + r;
-                    const int64_t base = ((int64_t)(t0 + min(i, n - 1)) * H + h) * DK + c;
+                    const int64_t row = t0 + min(i, n - 1);
+                    const int64_t base = (row * H + h) * DK + c;
+                    const int64_t kbase = (row * a.Hk + hk) * DK + c;
                     rg[r] = a.raw_gate[base];
-                    kk[r] = i < n ? ld_in<IN16>(a.k, base) : 0.f;
-                    qq[r] = (FW && i < n) ? ld_in<IN16>(a.q, base) : 0.f;
+                    kk[r] = i < n ? ld_in<IN16>(a.k, kbase) : 0.f;
+                    qq[r] = (FW && i < n) ? ld_in<IN16>(a.q, kbase) : 0.f;
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {

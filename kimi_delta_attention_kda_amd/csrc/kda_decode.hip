@@ -41,8 +41,9 @@ __global__ __launch_bounds__(NT) void kda_decode_kernel(DecodeArgs a) {
         float la = -expf(a.a_log[h]) * sp;
         if (a.gate_mode == 1) la = fmaxf(la, a.lb);
         sA[t] = expf(la);
-        sK[t] = ld((const T *)a.k + ((int64_t)b * a.H + h) * DK + t);
-        sQ[t] = ld((const T *)a.q + ((int64_t)b * a.H + h) * DK + t);
+        const int hk = h / (a.H / a.Hk);  // key head of value head h
+        sK[t] = ld((const T *)a.k + ((int64_t)b * a.Hk + hk) * DK + t);
+        sQ[t] = ld((const T *)a.q + ((int64_t)b * a.Hk + hk) * DK + t);
     }
     __syncthreads();
     if (t < 64) {  // q . k

@@ -109,7 +109,9 @@ __device__ __forceinline__ void pair_of_wave(int w, int pp, int &bI, int &bJ) {
     }
 }
 
-template <int DKT, int MODE>
+// GQA: fewer key heads than value heads (a.Hk < a.H); q and k rows then have their own
+// stride and head.  The equal-heads instantiation keeps one set of row offsets.
+template <int DKT, int MODE, bool GQA>
 __global__ __launch_bounds__(Geo<DKT>::NT, 512 / Geo<DKT>::NT) void kda_fast_kernel(ChainArgs a) {
     using L = Lds<DKT, MODE>;
     using Gm = Geo<DKT>;
@@ -215,6 +217,7 @@ __global__ __launch_bounds__(Geo<DKT>::NT, 512 / Geo<DKT>::NT) void kda_fast_ker
         }
         const int len = t_end - t_begin;
         if (FW && len <= 0) continue;
+        const int hk = GQA ? h / (H / a.Hk) : h;  // key head of value head h
         const int n_chunks = len > 0 ? (len + 63) / 64 : 0;
         const float negA = -expf(a.a_log[h]);
         const f32x4 dtb = *(const f32x4 *)(a.dt_bias + h * DK + c0) * 1.44269504088896341f;
@@ -246,18 +249,23 @@ __global__ __launch_bounds__(Geo<DKT>::NT, 512 / Geo<DKT>::NT) void kda_fast_ker
     // so the waves issuing them are not held up while every workgroup's loads drain.
     // Addresses: a scalar base per chunk (its first token, this head) plus 32-bit lane
     // offsets; the four row offsets of a chunk are formed once, at its first group.
-    unsigned roff[4];
+    unsigned roff[4], roffk[4];  // roffk: q/k rows (GQA only)
     auto issue = [&](int ck, int q) {
         const int t0 = t_begin + ck * 64;
         const int64_t rb = (int64_t)t0 * H + h;
+        const int64_t rbk = GQA ? (int64_t)t0 * a.Hk + hk : rb;
         if (q == 0) {
             const int n = min(64, t_end - t0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) roff[r] = (unsigned)(min(rbase + r, n - 1) * (H * DK) + c0);
+            for (int r = 0; r < 4; ++r) {
+                roff[r] = (unsigned)(min(rbase + r, n - 1) * (H * DK) + c0);
+                if constexpr (GQA) roffk[r] = (unsigned)(min(rbase + r, n - 1) * (a.Hk * DK) + c0);
+            }
         }
+        const unsigned *ko = GQA ? roffk : roff;
         const float *rg = a.raw_gate + rb * DK;
-        const bf16_t *kp = (const bf16_t *)a.k + rb * DK;
-        const bf16_t *qp = (const bf16_t *)a.q + rb * DK;
+        const bf16_t *kp = (const bf16_t *)a.k + rbk * DK;
+        const bf16_t *qp = (const bf16_t *)a.q + rbk * DK;
         const bf16_t *vp = (const bf16_t *)a.v + rb * DV;
         if (q == 0) {
             praw[0] = *(const f32x4 *)(rg + roff[0]);
@@ -268,17 +276,17 @@ __global__ __launch_bounds__(Geo<DKT>::NT, 512 / Geo<DKT>::NT) void kda_fast_ker
             pbl = a.beta_logits[rb + (unsigned)(min(l, t_end - t0 - 1) * H)];
         } else if (q == 2) {
 #pragma unroll
-            for (int r = 0; r < 3; ++r) pk[r] = *(const bf16x4 *)(kp + roff[r]);
+            for (int r = 0; r < 3; ++r) pk[r] = *(const bf16x4 *)(kp + ko[r]);
         } else if (q == 3) {
-            pk[3] = *(const bf16x4 *)(kp + roff[3]);
+            pk[3] = *(const bf16x4 *)(kp + ko[3]);
             if (FW) {
-                pq[0] = *(const bf16x4 *)(qp + roff[0]);
-                pq[1] = *(const bf16x4 *)(qp + roff[1]);
+                pq[0] = *(const bf16x4 *)(qp + ko[0]);
+                pq[1] = *(const bf16x4 *)(qp + ko[1]);
             }
         } else if (q == 4) {
             if (FW) {
-                pq[2] = *(const bf16x4 *)(qp + roff[2]);
-                pq[3] = *(const bf16x4 *)(qp + roff[3]);
+                pq[2] = *(const bf16x4 *)(qp + ko[2]);
+                pq[3] = *(const bf16x4 *)(qp + ko[3]);
             }
             if (has_v) pv[0] = *(const bf16x4 *)(vp + roff[0]);
         } else {
@@ -640,13 +648,20 @@ __global__ __launch_bounds__(Geo<DKT>::NT, 512 / Geo<DKT>::NT) void kda_fast_ker
 }  // namespace fast
 
 namespace {
-template <int DKT>
-void launch_fast_dk(const ChainArgs &a, int mode, dim3 grid, hipStream_t stream) {
+template <int DKT, bool GQA>
+void launch_fast_dk_g(const ChainArgs &a, int mode, dim3 grid, hipStream_t stream) {
     const dim3 block(fast::Geo<DKT>::NT);
     if (mode == MODE_FWD)
-        hipLaunchKernelGGL((fast::kda_fast_kernel<DKT, MODE_FWD>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((fast::kda_fast_kernel<DKT, MODE_FWD, GQA>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((fast::kda_fast_kernel<DKT, MODE_SUMMARY>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((fast::kda_fast_kernel<DKT, MODE_SUMMARY, GQA>), grid, block, 0, stream, a);
+}
+template <int DKT>
+void launch_fast_dk(const ChainArgs &a, int mode, dim3 grid, hipStream_t stream) {
+    if (a.Hk != a.H)
+        launch_fast_dk_g<DKT, true>(a, mode, grid, stream);
+    else
+        launch_fast_dk_g<DKT, false>(a, mode, grid, stream);
 }
 }  // namespace
 

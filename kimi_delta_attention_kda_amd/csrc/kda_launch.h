@@ -37,8 +37,8 @@ struct PlanLayout {
 PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_slots);
 
 struct ChainArgs {
-    const void *q;                // [T,H,dk] (FWD only)
-    const void *k;                // [T,H,dk]
+    const void *q;                // [T,Hk,dk] (FWD only)
+    const void *k;                // [T,Hk,dk]
     const void *v;                // [T,H,dv]
     const float *raw_gate;        // [T,H,dk]
     const float *beta_logits;     // [T,H]
@@ -51,7 +51,8 @@ struct ChainArgs {
     float *M;                     // SUMMARY [n_seg,H,dk,dk]
     float *U;                     // SUMMARY [n_seg,H,dk,dv]
     int n_items;                  // B or n_seg
-    int H;
+    int H;                        // value heads
+    int Hk;                       // key heads (q, k); value head h reads key head h / (H / Hk)
     int n_slices;                 // value slices per (item, head)
     int gate_mode;
     float lb;
@@ -93,7 +94,7 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
                               hipStream_t stream);
 
 struct DecodeArgs {
-    const void *q, *k, *v;        // [B, H, dk] / [B, H, dv], one token per sequence
+    const void *q, *k, *v;        // [B, Hk, dk] / [B, H, dv], one token per sequence
     const float *raw_gate;        // [B, H, dk]
     const float *beta_logits;     // [B, H]
     const float *a_log;           // [H]
@@ -101,7 +102,7 @@ struct DecodeArgs {
     float *state_pool;            // [slots, H, dk, dv] (or [.., dv, dk] when v_first)
     const int32_t *state_indices; // [B]
     void *out;                    // [B, H, dv]
-    int B, H;
+    int B, H, Hk;                 // value heads H, key heads Hk (dividing H)
     int gate_mode;
     float lb;
     int beta_mode;

@@ -52,10 +52,15 @@ class Workload:
     raw_mean: float = 0.0     # raw_gate ~ N(raw_mean, 1)
     beta_mean: float = 0.0    # beta_logits ~ N(beta_mean, beta_sigma^2)
     a_log_hi: float = math.log(16.0)  # a_log ~ U(0, a_log_hi)
+    Hk: int = 0               # key heads of q and k (0: as many as value heads H)
 
     @property
     def T(self) -> int:
         return int(sum(self.lengths))
+
+    @property
+    def HK(self) -> int:
+        return self.Hk or self.H
 
     @property
     def B(self) -> int:
@@ -126,7 +131,7 @@ def make_inputs(w: Workload, device="cpu") -> dict:
     """Draws every tensor of workload `w` on `device` (deterministic per device).
 
     Returns a dict of torch tensors in the library's layouts:
-      q, k [T,H,dk]; v [T,H,dv] (dtype per workload); raw_gate [T,H,dk] f32;
+      q, k [T,Hk,dk]; v [T,H,dv] (dtype per workload); raw_gate [T,H,dk] f32;
       beta_logits [T,H] f32; a_log [H] f32; dt_bias [H,dk] f32;
       cu_seqlens [B+1] int32; state_pool [n_slots,H,dk,dv] f32;
       state_indices [B] int32; plus host copies of lengths/indices.
@@ -143,8 +148,8 @@ def make_inputs(w: Workload, device="cpu") -> dict:
     def unit_rows(x):
         return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True).clamp_min(1e-30)
 
-    q = unit_rows(normal(T, H, dk)).to(dt)
-    k = unit_rows(normal(T, H, dk)).to(dt)
+    q = unit_rows(normal(T, w.HK, dk)).to(dt)
+    k = unit_rows(normal(T, w.HK, dk)).to(dt)
     v = normal(T, H, dv).to(dt)
     raw_gate = normal(T, H, dk) + w.raw_mean
     beta_logits = normal(T, H, std=w.beta_sigma) + w.beta_mean

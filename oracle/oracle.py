@@ -155,8 +155,13 @@ def scan(M, U, S_init):
 # ----------------------------------------------------------- from inputs --
 
 def item_from_inputs(inp: dict, b: int, h: int, with_q=True, t0=None, t1=None, S0=None):
-    """Slices sequence b, head h of a workload's inputs (torch tensors) into
-    fp64 numpy arrays for the oracle.  t0/t1 bound the token range (absolute)."""
+    """Slices sequence b, value head h of a workload's inputs (torch tensors) into
+    fp64 numpy arrays for the oracle.  t0/t1 bound the token range (absolute).
+
+    q and k have Hk key heads, everything else H value heads (max.nn.state_space.kda_chunk,
+    Parameters); Hk divides H and value head h reads key head h // (H // Hk), so that each
+    key head serves a run of consecutive value heads (the reading taken where the page
+    leaves the grouping open)."""
     cu = inp["cu"]
     a, e = cu[b], cu[b + 1]
     if t0 is not None:
@@ -164,13 +169,17 @@ def item_from_inputs(inp: dict, b: int, h: int, with_q=True, t0=None, t1=None, S
     if t1 is not None:
         e = t1
 
-    def sl(name):
-        return inp[name][a:e, h].detach().to("cpu", dtype=__import__("torch").float64).numpy()
+    H, Hk = inp["v"].shape[1], inp["k"].shape[1]
+    assert H % Hk == 0
+    hk = h // (H // Hk)
+
+    def sl(name, head=h):
+        return inp[name][a:e, head].detach().to("cpu", dtype=__import__("torch").float64).numpy()
 
     if S0 is None:
         slot = inp["indices"][b]
         S0 = inp["state_pool"][slot, h].detach().to("cpu").double().numpy()
-    return dict(q=sl("q") if with_q else None, k=sl("k"), v=sl("v"), raw_gate=sl("raw_gate"),
+    return dict(q=sl("q", hk) if with_q else None, k=sl("k", hk), v=sl("v"), raw_gate=sl("raw_gate"),
                 beta_in=sl("beta_logits"),
                 dt_bias=inp["dt_bias"][h].detach().cpu().double().numpy(),
                 a_log=float(inp["a_log"][h].item()), S0=S0)

@@ -33,6 +33,13 @@ def test_prefill_algorithmic_flops_varlen_32k():
     assert round(bench.algorithmic_flops(w) / 1e9, 1) == 146.0
 
 
+def test_grouped_key_heads_read_q_and_k_once_per_key_head():
+    w = wl.custom([100, 28], H=8, Hk=2, dk=64, dv=64, dtype="bf16", gate_mode=1)
+    per_token = 8 * (64 * 2 + 64 * 2 + 64 * 4 + 4) + 2 * (2 * 64 * 2)  # v out raw beta; q k
+    slots = 2 * 2 * (8 * 64 * 64 * 4)
+    assert bench.algorithmic_bytes(w) == 128 * per_token + slots + 8 * 65 * 4 + 3 * 4 + 2 * 4
+
+
 def test_decode_compulsory_bytes():
     w = wl.workload("decode_512")
     assert (w.B, w.T, w.H, w.dk, w.dv) == (512, 512, 32, 128, 128)

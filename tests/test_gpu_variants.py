@@ -1,10 +1,11 @@
-"""GPU parity of the contract variants: single-token decode, the V_FIRST pool layout and
-beta given as a probability.
+"""GPU parity of the contract variants: single-token decode, the V_FIRST pool layout,
+beta given as a probability, and fewer key heads than value heads.
 
 Decode is compared with the fp64 oracle's token recurrence (one token per sequence, on
 every (sequence, head)); V_FIRST must reproduce the K_FIRST results bit for bit (only
 the addressing of the pool slots differs); probability-mode beta is compared with the
-oracle on every (sequence, head).
+oracle on every (sequence, head).  With Hk < H key heads, every call must equal, bit for
+bit, the equal-heads call on q and k repeated per value head, and the oracle.
 """
 import pytest
 import torch
@@ -103,3 +104,85 @@ def test_prefill_beta_probability(dtype, dk):
     print(f"  out_err={eo:.3e} state_err={es:.3e}", flush=True)
     assert eo <= (OUT_TOL_BF16 if dtype == "bf16" else OUT_TOL_F32)
     assert es <= STATE_TOL
+
+
+def _expand_heads(inp, H):
+    """q and k repeated so that value head h has its own copy of key head h // (H // Hk)."""
+    e = dict(inp)
+    g = H // inp["k"].shape[1]
+    e["q"] = inp["q"].repeat_interleave(g, dim=1).contiguous()
+    e["k"] = inp["k"].repeat_interleave(g, dim=1).contiguous()
+    return e
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
+@pytest.mark.parametrize("dtype,dk,Hk,workspace", [("bf16", 128, 2, "torch"), ("bf16", 128, 1, "none"),
+                                                   ("bf16", 64, 2, "torch"), ("f32", 64, 2, "torch"),
+                                                   ("f32", 128, 1, "torch")])
+def test_prefill_grouped_key_heads(dtype, dk, Hk, workspace):
+    """H = 4 value heads over Hk key heads.  The 3,000-token sequence is split into pieces
+    by the balanced bf16 dk = 128 pass."""
+    from kda_testlib import compare_items, run_fwd, untouched_slots_identical
+    from kda_testlib import OUT_TOL_BF16, OUT_TOL_F32, STATE_TOL
+    w = wl.custom([3000, 70, 0, 129, 1], H=4, Hk=Hk, dk=dk, dv=dk, dtype=dtype, gate_mode=1, seed=23,
+                  name="gqa")
+    print(f"[case] prefill {dtype} dk={dk} H=4 Hk={Hk} workspace={workspace}", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+    assert inp["q"].shape[1] == Hk and inp["v"].shape[1] == 4
+    out, pool = run_fwd(w, inp, workspace=workspace)
+    out_e, pool_e = run_fwd(w, _expand_heads(inp, w.H), workspace=workspace)
+    assert torch.equal(_bits(out), _bits(out_e))
+    assert torch.equal(_bits(pool), _bits(pool_e))
+    assert untouched_slots_identical(inp, pool)
+    eo, es = compare_items(w, inp, out, pool, [(b, h) for b in range(w.B) for h in range(w.H)])
+    print(f"  out_err={eo:.3e} state_err={es:.3e}", flush=True)
+    assert eo <= (OUT_TOL_BF16 if dtype == "bf16" else OUT_TOL_F32) and es <= STATE_TOL
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64)])
+def test_decode_grouped_key_heads(dtype, dk):
+    from kda_testlib import compare_items, OUT_TOL_BF16, OUT_TOL_F32, STATE_TOL
+    B = 9
+    w = wl.custom([1] * B, H=8, Hk=2, dk=dk, dv=dk, dtype=dtype, gate_mode=1, name="decode_gqa",
+                  n_slots=2 * B, state_sigma=0.05)
+    print(f"[case] decode {dtype} dk={dk} H=8 Hk=2", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+    pool = inp["state_pool"].clone()
+    out = _decode(w, inp, pool)
+    pool_e = inp["state_pool"].clone()
+    out_e = _decode(w, _expand_heads(inp, w.H), pool_e)
+    assert torch.equal(_bits(out), _bits(out_e)) and torch.equal(_bits(pool), _bits(pool_e))
+    eo, es = compare_items(w, inp, out.view(B, w.H, dk), pool, [(b, h) for b in range(B) for h in range(w.H)])
+    print(f"  out_err={eo:.3e} state_err={es:.3e}", flush=True)
+    assert eo <= (OUT_TOL_BF16 if dtype == "bf16" else OUT_TOL_F32) and es <= STATE_TOL
+
+
+@pytest.mark.parametrize("dtype,dk,gate", [("bf16", 128, 1), ("bf16", 64, 0), ("f32", 128, 0)])
+def test_segment_summary_grouped_key_heads(dtype, dk, gate):
+    w = wl.custom([3 * 300], H=4, Hk=2, dk=dk, dv=dk, dtype=dtype, gate_mode=gate, seed=24,
+                  name="seg_gqa", n_slots=1, segments=3, raw_mean=-6.0, a_log_hi=0.0, beta_mean=-4.0)
+    print(f"[case] segment summaries {dtype} dk={dk} gate_mode={gate} H=4 Hk=2", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+
+    def summ(x):
+        M, U = kda.segment_summary(x["k"], x["v"], x["raw_gate"], x["beta_logits"], x["a_log"],
+                                   x["dt_bias"], x["seg_offsets"], gate_mode=_gate(w),
+                                   lower_bound=w.lower_bound)
+        torch.cuda.synchronize()
+        return M, U
+
+    M, U = summ(inp)
+    M_e, U_e = summ(_expand_heads(inp, w.H))
+    assert torch.equal(_bits(M), _bits(M_e)) and torch.equal(_bits(U), _bits(U_e))
+    from oracle import oracle as orc
+    from kda_testlib import rel_fro, STATE_TOL
+    offs = inp["seg_offsets"].tolist()
+    pairs = [(i, h) for i in range(3) for h in range(w.H)]
+    its = [orc.item_from_inputs(inp, 0, h, with_q=False, t0=offs[i], t1=offs[i + 1]) for (i, h) in pairs]
+    for (i, h), (M_ref, U_ref) in zip(pairs, orc.segment_maps(its, w.dk, w.dv, w.gate_mode, w.lower_bound,
+                                                               w.beta_mode)):
+        assert rel_fro(wl.as_f64(M[i, h]), M_ref) <= STATE_TOL
+        assert rel_fro(wl.as_f64(U[i, h]), U_ref) <= STATE_TOL

@@ -184,6 +184,56 @@ def test_python_binding_checks_before_the_library():
                       torch.zeros(1, dtype=torch.int32))
     with pytest.raises(ValueError):   # at least one segment
         kda.context_parallel(torch.zeros(0, 16, 16), torch.zeros(0, 16, 16), torch.zeros(16, 16))
+    q3 = torch.zeros(T, 3, dk, dtype=torch.bfloat16)
+    v4 = torch.zeros(T, 4, dk, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):   # 3 key heads do not divide 4 value heads
+        kda.chunk_fwd(q3, q3, v4, torch.zeros(T, 4, dk), torch.zeros(T, 4), torch.zeros(4),
+                      torch.zeros(4, dk), torch.tensor([0, T], dtype=torch.int32),
+                      torch.zeros(1, 4, dk, dk), torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        kda.decode(q3, q3, v4, torch.zeros(T, 4, dk), torch.zeros(T, 4), torch.zeros(4),
+                   torch.zeros(4, dk), torch.zeros(T, 4, dk, dk), torch.zeros(T, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        kda.segment_summary(q3, v4, torch.zeros(T, 4, dk), torch.zeros(T, 4), torch.zeros(4),
+                            torch.zeros(4, dk), torch.tensor([0, T], dtype=torch.int32))
+
+
+def test_key_heads_must_divide_value_heads(L):
+    for hk in (3, -1, 5):
+        d = _desc()
+        d.num_key_heads = hk
+        assert _fwd(L, d) == ESHAPE
+        assert _fwd_ws(L, d) == ESHAPE
+        assert L.kda_segment_summary(C.byref(d), *([FAKE] * 7), 2, FAKE, FAKE, None) == ESHAPE
+    d = _desc(T=4, B=4)
+    d.num_key_heads = 3
+    assert _dec(L, d) == ESHAPE
+    # 0 means as many key heads as value heads; 1, 2 and 4 divide H = 4 (nothing to launch: B = 0)
+    for hk in (0, 1, 2, 4):
+        d = _desc(B=0)
+        d.num_key_heads = hk
+        assert _fwd(L, d) == OK
+
+
+def test_descriptor_layout_matches_the_header(tmp_path):
+    """The binding's ctypes descriptor has the size and field offsets the C compiler gives
+    kda_desc in include/libkda.h."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    names = [f[0] for f in kda.KdaDesc._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"libkda.h\"\nint main(void) {\n"
+                   + '  printf("%zu\\n", sizeof(kda_desc));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(kda_desc, {n}));\n' for n in names)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(root, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == C.sizeof(kda.KdaDesc)
+    assert got[1:] == [getattr(kda.KdaDesc, n).offset for n in names]
 
 
 def test_missing_library_fails_loudly(monkeypatch):

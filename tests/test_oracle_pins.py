@@ -220,6 +220,24 @@ def test_forward_items_equals_gate_then_recurrence_threads():
         assert np.allclose(S, wS, rtol=1e-13, atol=1e-15) and np.allclose(o, wo, rtol=1e-13, atol=1e-15)
 
 
+def test_grouped_key_heads_follow_their_group():
+    """kda_chunk lays q and k over key heads and everything else over value heads.  With
+    H = 4 value heads and Hk = 2 key heads, value heads 0 and 1 read key head 0, value
+    heads 2 and 3 key head 1; gates, values and the state stay per value head."""
+    from kimi_delta_attention_kda_amd import workloads as wl
+    w = wl.custom([5, 3], H=4, Hk=2, dk=8, dv=8, dtype="f32", gate_mode=1, seed=3)
+    inp = wl.make_inputs(w)
+    assert inp["q"].shape[1] == 2 and inp["v"].shape[1] == 4
+    a, e = inp["cu"][1], inp["cu"][2]
+    for h, key_head in zip(range(4), (0, 0, 1, 1)):
+        it = orc.item_from_inputs(inp, 1, h)
+        assert np.array_equal(it["k"], inp["k"][a:e, key_head].double().numpy())
+        assert np.array_equal(it["q"], inp["q"][a:e, key_head].double().numpy())
+        assert np.array_equal(it["v"], inp["v"][a:e, h].double().numpy())
+        assert np.array_equal(it["raw_gate"], inp["raw_gate"][a:e, h].double().numpy())
+        assert np.array_equal(it["S0"], inp["state_pool"][inp["indices"][1], h].double().numpy())
+
+
 # ------------------------------------------------------------ chunk form --
 
 @pytest.mark.parametrize("chunk", [1, 2, 5, 16, 64])
