@@ -122,8 +122,9 @@ kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, con
                          const int32_t *state_indices, void *out, void *stream);
 
 /*
- * kda_chunk_fwd with a caller-owned workspace.  For bf16 with dk = dv = 128
- * the forward pass is load-balanced over the GPU's compute units: a sequence
+ * kda_chunk_fwd with a caller-owned workspace.  For bf16 with the safe gate
+ * (bound >= -5.3, dk = dv in {64, 128}) the forward pass is load-balanced over
+ * the GPU's compute units: a sequence
  * much longer than the average load per CU is cut into pieces at chunk
  * boundaries that run in parallel, using the segment maps of KDA Context
  * Parallelism (Theory: a piece started from state X ends in M X + U, and its

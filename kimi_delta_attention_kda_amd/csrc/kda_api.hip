@@ -108,10 +108,7 @@ hipMemPool_t device_pool(int dev) {
     return pools[dev];
 }
 
-// The balanced schedule (planner, piece scan, fixup) is built for dk = dv = 128.
-bool planned_applies(const kda_desc *d) {
-    return use_fast(d) && d->dk == 128 && d->batch > 0 && d->total_tokens > 0;
-}
+bool planned_applies(const kda_desc *d) { return use_fast(d) && d->batch > 0 && d->total_tokens > 0; }
 
 // chunk kernel of the bf16 dk = dv = 128 forward pass
 const kda::FwdKernel &fwd_kernel() { return kda::FWD64; }
@@ -225,7 +222,7 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
             st = workspace_bytes_for(desc, &need, &lay, &n_cu);
             if (st != KDA_OK) return st;
             if (workspace_bytes < need) return KDA_ERR_SHAPE;
-            e = kda::launch_planned_fwd(a, (char *)workspace, lay, n_cu, fwd_kernel(), (hipStream_t)stream);
+            e = kda::launch_planned_fwd(a, desc->dk, (char *)workspace, lay, n_cu, fwd_kernel(), (hipStream_t)stream);
         } else {
             e = kda::launch_fast(a, desc->dk, kda::MODE_FWD, (hipStream_t)stream);
         }

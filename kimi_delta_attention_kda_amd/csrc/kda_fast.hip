@@ -677,10 +677,15 @@ hipError_t launch_fast(const ChainArgs &a, int dk, int mode, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_fast_planned(const ChainArgs &a, int n_cu, hipStream_t stream) {
+hipError_t launch_fast_planned(const ChainArgs &a, int dk, int n_cu, hipStream_t stream) {
     // persistent: one workgroup per CU (LDS allows no second one), drained queues end it
     const dim3 grid(8 * ((n_cu + 7) / 8));
-    launch_fast_dk<128>(a, MODE_FWD, grid, stream);
+    if (dk == 128)
+        launch_fast_dk<128>(a, MODE_FWD, grid, stream);
+    else if (dk == 64)
+        launch_fast_dk<64>(a, MODE_FWD, grid, stream);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -79,9 +79,10 @@ hipError_t launch_chain(const ChainArgs &a, int dk, bool bf16_in, int mode, hipS
 // segment summaries (n_slices = 2).
 hipError_t launch_fast(const ChainArgs &a, int dk, int mode, hipStream_t stream);
 // forward pass over the queues of a plan (a.plan set), one persistent workgroup per CU
-hipError_t launch_fast_planned(const ChainArgs &a, int n_cu, hipStream_t stream);
-// The chunk kernel of the bf16 dk = dv = 128 forward pass: its chunk length and how many of
-// its workgroups share a CU (the planner sizes pieces in its chunks, for that many slots).
+hipError_t launch_fast_planned(const ChainArgs &a, int dk, int n_cu, hipStream_t stream);
+// The chunk kernel of the bf16 forward pass: its chunk length and how many of its
+// workgroups share a CU (the planner sizes pieces in its chunks, for that many slots).
+// LDS admits one workgroup per CU at dk = 128 (155 KB) and at dk = 64 (92 KB).
 struct FwdKernel {
     int chunk;
     int per_cu;
@@ -89,9 +90,9 @@ struct FwdKernel {
 constexpr FwdKernel FWD64 = {64, 1};  // kda_fast.hip
 
 // Planner, piece-state scan and output correction of the load-balanced forward pass
-// (bf16, dk = dv = 128).  ws is the workspace laid out by plan_layout.
-hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int n_cu, const FwdKernel &fk,
-                              hipStream_t stream);
+// (bf16, dk = dv in {64, 128}).  ws is the workspace laid out by plan_layout.
+hipError_t launch_planned_fwd(ChainArgs a, int dk, char *ws, const PlanLayout &lay, int n_cu,
+                              const FwdKernel &fk, hipStream_t stream);
 
 struct DecodeArgs {
     const void *q, *k, *v;        // [B, Hk, dk] / [B, H, dv], one token per sequence

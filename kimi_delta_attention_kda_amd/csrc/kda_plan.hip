@@ -1,5 +1,5 @@
 // kda_plan.hip -- load-balanced forward pass: long sequences are cut into pieces that
-// run in parallel (bf16, dk = dv = 128).
+// run in parallel (bf16, dk = dv in {64, 128}).
 //
 // A (sequence, head) chain is sequential, so one long sequence would bound the kernel
 // while short ones leave their CUs idle.  The context-parallel construction of the "KDA
@@ -35,7 +35,6 @@ constexpr int NBIN = 1024; // length bins of the longest-first order
 constexpr int L_MIN = 4;   // shortest first piece worth a split, in chunks
 constexpr int NCACHE = 4096;  // sequences whose chunk counts the planner keeps in LDS
 constexpr int ECACHE = 1024;  // entities the planner keeps in LDS
-constexpr int DK = 128, DV = 128;
 
 static_assert(NBIN == PT, "one bin per planner thread");
 
@@ -377,75 +376,79 @@ struct PieceArgs {
 // Incoming states of the later pieces, in order, and the final state into the slot.
 // Task = (split sequence, head, 16-column block): X_{k+1} = M_k X_k + U_k on those
 // columns with fp32 16x16x4 MFMAs (products and sums in fp32, as the recurrence needs).
-// Wave w owns rows 32w .. 32w+31 (two 16-row tiles); lane (g, li) holds rows
-// 32w + 16tt + 4g + s of column li, the accumulator layout.  The contraction index of
-// MFMA step kk on lane quarter g is 32g + kk, so a lane's A operands are 32 consecutive
-// entries of one row of M_k (eight 16-byte loads) and its B operands one column of X_k
-// from LDS, skewed by 16 floats per 32 rows so the four quarters read distinct banks.
+// Wave w owns rows RW w .. RW w + RW - 1 (RW = dk/4: TT = dk/64 tiles of 16 rows); lane
+// (g, li) holds rows RW w + 16tt + 4g + s of column li, the accumulator layout.  The
+// contraction index of MFMA step kk on lane quarter g is KQ g + kk (KQ = dk/4), so a
+// lane's A operands are KQ consecutive entries of one row of M_k (16-byte loads) and its
+// B operands one column of X_k from LDS, skewed by 16 floats per quarter so the four
+// quarters read distinct banks.
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ int sx_at(int k, int c) { return 16 * k + c + 16 * (k >> 5); }
+template <int DK>
+__device__ __forceinline__ int sx_at(int k, int c) { return 16 * k + c + 16 * (k / (DK / 4)); }
 
+template <int DK>
 __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
-    __shared__ float sx[16 * DK + 16 * (DK / 32)];
+    constexpr int DV = DK, TT = DK / 64, RW = DK / 4, KQ = DK / 4, NCB = DV / 16;
+    __shared__ float sx[16 * DK + 16 * 4];
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
     const int H = p.H;
-    const int n_tasks = p.hdr->n_split * H * (DV / 16);
-    // The 8 column blocks of one (sequence, head) read the same M_k: keep them on one XCD
+    const int n_tasks = p.hdr->n_split * H * NCB;
+    // The column blocks of one (sequence, head) read the same M_k: keep them on one XCD
     // (workgroups are dealt to the XCDs round-robin), so M_k comes from HBM once.
-    for (int lin = blockIdx.x; lin < ((n_tasks + 63) & ~63); lin += gridDim.x) {
-        const int cb = (lin >> 3) & 7, jh = ((lin >> 6) << 3) | (lin & 7);
+    for (int lin = blockIdx.x; lin < (n_tasks + 8 * NCB - 1) / (8 * NCB) * (8 * NCB); lin += gridDim.x) {
+        const int cb = (lin >> 3) % NCB, jh = (lin / (8 * NCB)) * 8 + (lin & 7);
         if (jh >= p.hdr->n_split * H) continue;  // uniform over the workgroup
         const int h = jh % H, j = jh / H;
         const int4 sq = p.sseq[j];
         const int col = 16 * cb + li;
         float *slot = p.state_pool + ((int64_t)sq.w * H + h) * DK * DV;
-        // X_k of this lane: rows 32w + 16tt + 4g + s, column col
-        f32x4 x[2];
+        // X_k of this lane: rows RW w + 16tt + 4g + s, column col
+        f32x4 x[TT];
         auto slot_at = [&](int r) -> float & { return p.v_first ? slot[col * DK + r] : slot[r * DV + col]; };
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) x[tt][s] = slot_at(32 * w + 16 * tt + 4 * g + s);
+            for (int s = 0; s < 4; ++s) x[tt][s] = slot_at(RW * w + 16 * tt + 4 * g + s);
         for (int i = 0; i < sq.z; ++i) {
             const int64_t kh = (int64_t)(sq.y + i) * H + h;
             // M_k rows and U_k entries are independent of X_k: issue them first
-            f32x4 ma[2][8], acc[2];
+            f32x4 ma[TT][KQ / 4], acc[TT];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const float *Mr = p.M + kh * DK * DK + (int64_t)(32 * w + 16 * tt + li) * DK + 32 * g;
+            for (int tt = 0; tt < TT; ++tt) {
+                const float *Mr = p.M + kh * DK * DK + (int64_t)(RW * w + 16 * tt + li) * DK + KQ * g;
 #pragma unroll
-                for (int q = 0; q < 8; ++q) ma[tt][q] = *(const f32x4 *)(Mr + 4 * q);
-                const float *Ur = p.U + kh * DK * DV + (int64_t)(32 * w + 16 * tt + 4 * g) * DV + col;
+                for (int q = 0; q < KQ / 4; ++q) ma[tt][q] = *(const f32x4 *)(Mr + 4 * q);
+                const float *Ur = p.U + kh * DK * DV + (int64_t)(RW * w + 16 * tt + 4 * g) * DV + col;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) acc[tt][s] = Ur[s * DV];
             }
             // the correction's MFMA reads X_k^T rows (one column of X_k) as bf16
-            bf16_t *xt = p.XT + kh * DV * DK + (int64_t)col * DK + 32 * w + 4 * g;
+            bf16_t *xt = p.XT + kh * DV * DK + (int64_t)col * DK + RW * w + 4 * g;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) *(bf16x4 *)(xt + 16 * tt) = bf4(x[tt]);
+            for (int tt = 0; tt < TT; ++tt) *(bf16x4 *)(xt + 16 * tt) = bf4(x[tt]);
             __syncthreads();  // every wave is done reading the previous X from LDS
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) sx[sx_at(32 * w + 16 * tt + 4 * g + s, li)] = x[tt][s];
+                for (int s = 0; s < 4; ++s) sx[sx_at<DK>(RW * w + 16 * tt + 4 * g + s, li)] = x[tt][s];
             __syncthreads();
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
+            for (int q = 0; q < KQ / 4; ++q)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float bx = sx[sx_at(32 * g + 4 * q + e, li)];
-                    acc[0] = mfma_f32(ma[0][q][e], bx, acc[0]);
-                    acc[1] = mfma_f32(ma[1][q][e], bx, acc[1]);
+                    const float bx = sx[sx_at<DK>(KQ * g + 4 * q + e, li)];
+#pragma unroll
+                    for (int tt = 0; tt < TT; ++tt) acc[tt] = mfma_f32(ma[tt][q][e], bx, acc[tt]);
                 }
-            x[0] = acc[0];
-            x[1] = acc[1];
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) x[tt] = acc[tt];
         }
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) slot_at(32 * w + 16 * tt + 4 * g + s) = x[tt][s];
+            for (int s = 0; s < 4; ++s) slot_at(RW * w + 16 * tt + 4 * g + s) = x[tt][s];
         __syncthreads();
     }
 }
@@ -454,14 +457,16 @@ __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
 // numbered piece-major; a workgroup takes FIX_TASKS consecutive tasks (mostly one piece
 // and head), decodes them from the piece table staged once in LDS, and stages X_k^T (bf16,
 // written by piece_scan_kernel) in LDS when the piece or head changes.  Wave w owns the
-// 16 tokens 16w .. 16w+15 of the chunk and all 128 columns, C^T = X^T W^T with 16x16x32
+// 16 tokens 16w .. 16w+15 of the chunk and all dv columns, C^T = X^T W^T with 16x16x32
 // bf16 MFMAs: each W row is read once, and a lane adds 4 consecutive columns of one token
 // per column tile (8-byte read-modify-writes).
 constexpr int FIX_NP = 256;   // pieces staged in LDS (more: read from global memory)
-constexpr int FIX_XP = DK + 8;  // bf16 pitch of the staged X^T rows
-constexpr int FIX_TASKS = 4;    // tasks per group (1, 2 and 4 measured within 10% of each other)
+constexpr int FIX_TASKS = 4;  // tasks per group (1, 2 and 4 measured within 10% of each other)
 
+template <int DK>
 __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
+    constexpr int DV = DK;
+    constexpr int FIX_XP = DK + 8;  // bf16 pitch of the staged X^T rows
     __shared__ int4 spc[FIX_NP];
     __shared__ __attribute__((aligned(16))) bf16_t sxt[DV * FIX_XP];
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
@@ -494,12 +499,12 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         // this wave's loads first; rows past the chunk's end repeat its last row and are
         // not stored (a wave past the end of a short chunk only joins the barriers)
         const int64_t rowh = (int64_t)(t0 + min(16 * w + li, n - 1)) * H + h;
-        bf16x8 bw[4];
-        bf16x4 ov[8];
+        bf16x8 bw[DK / 32];
+        bf16x4 ov[DV / 16];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) bw[kb] = *(const bf16x8 *)(p.W + rowh * DV + 32 * kb + 8 * g);
+        for (int kb = 0; kb < DK / 32; ++kb) bw[kb] = *(const bf16x8 *)(p.W + rowh * DK + 32 * kb + 8 * g);
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) ov[ct] = *(const bf16x4 *)(p.out + rowh * DV + 16 * ct + 4 * g);
+        for (int ct = 0; ct < DV / 16; ++ct) ov[ct] = *(const bf16x4 *)(p.out + rowh * DV + 16 * ct + 4 * g);
         if (key != cur) {  // uniform over the workgroup
             __syncthreads();  // every wave is done with the previous X^T
             const bf16_t *xt = p.XT + (int64_t)key * DV * DK;
@@ -514,10 +519,10 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         const bool store = 16 * w + li < n;
         bf16_t *o = p.out + ((int64_t)(t0 + 16 * w + li) * H + h) * DV + 4 * g;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
+        for (int ct = 0; ct < DV / 16; ++ct) {
             f32x4 acc = f4(ov[ct]);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < DK / 32; ++kb)
                 acc = mfma(*(const bf16x8 *)(sxt + (16 * ct + li) * FIX_XP + 32 * kb + 8 * g), bw[kb], acc);
             if (store) *(bf16x4 *)(o + 16 * ct) = bf4(acc);
         }
@@ -561,8 +566,9 @@ PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_slots) {
     return y;
 }
 
-hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int n_cu, const FwdKernel &fk,
-                              hipStream_t stream) {
+hipError_t launch_planned_fwd(ChainArgs a, int dk, char *ws, const PlanLayout &lay, int n_cu,
+                              const FwdKernel &fk, hipStream_t stream) {
+    if (dk != 64 && dk != 128) return hipErrorInvalidValue;
     plan::PlanArgs pa;
     pa.cu = a.offsets;
     pa.state_indices = a.state_indices;
@@ -591,7 +597,7 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     a.ws_M = (float *)(ws + lay.M);
     a.ws_U = (float *)(ws + lay.U);
     a.ws_W = ws + lay.W;
-    e = launch_fast_planned(a, fk.per_cu * n_cu, stream);
+    e = launch_fast_planned(a, dk, fk.per_cu * n_cu, stream);
     if (e != hipSuccess) return e;
 
     plan::PieceArgs pp;
@@ -611,11 +617,18 @@ hipError_t launch_planned_fwd(ChainArgs a, char *ws, const PlanLayout &lay, int 
     pp.cs = fk.chunk;
     // grids sized from capacities (the counts are known on the device only): every scan
     // task of a full plan at once; surplus workgroups find no task and exit
-    const int scan_grid = min((lay.np_cap * a.H * (plan::DV / 16) + 63) & ~63, 4 * n_cu);
-    hipLaunchKernelGGL(plan::piece_scan_kernel, dim3(scan_grid), dim3(256), 0, stream, pp);
+    const int ncb = dk / 16;  // 16-column blocks of the state
+    const int scan_grid = min((lay.np_cap * a.H * ncb + 8 * ncb - 1) / (8 * ncb) * (8 * ncb), 4 * n_cu);
+    if (dk == 128)
+        hipLaunchKernelGGL(plan::piece_scan_kernel<128>, dim3(scan_grid), dim3(256), 0, stream, pp);
+    else
+        hipLaunchKernelGGL(plan::piece_scan_kernel<64>, dim3(scan_grid), dim3(256), 0, stream, pp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(plan::fixup_kernel, dim3(4 * n_cu), dim3(256), 0, stream, pp);
+    if (dk == 128)
+        hipLaunchKernelGGL(plan::fixup_kernel<128>, dim3(4 * n_cu), dim3(256), 0, stream, pp);
+    else
+        hipLaunchKernelGGL(plan::fixup_kernel<64>, dim3(4 * n_cu), dim3(256), 0, stream, pp);
     return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-"""GPU parity of the load-balanced forward pass (bf16, dk = dv = 128).
+"""GPU parity of the load-balanced forward pass (bf16, safe gate, dk = dv in {64, 128}).
 
 Long sequences are cut into pieces whose transition and contribution chains run in
 parallel; their states are composed in order and the outputs corrected.  These tests
@@ -91,12 +91,13 @@ def _compare_all(w, inp, out, pool):
     assert es <= STATE_TOL
 
 
-@pytest.mark.parametrize("lengths", [(4096,), (3000, 100, 5000, 0, 64, 777)])
-def test_many_pieces_against_oracle(lengths):
+@pytest.mark.parametrize("lengths,dk", [((4096,), 128), ((3000, 100, 5000, 0, 64, 777), 128),
+                                        ((4096,), 64), ((3000, 100, 5000, 0, 64, 777), 64)])
+def test_many_pieces_against_oracle(lengths, dk):
     """Few chains on many CUs: every long sequence becomes many pieces."""
     from kda_testlib import untouched_slots_identical
-    w = wl.custom(lengths, H=2, dk=128, dv=128, name="pieces")
-    print(f"[case] pieces lengths={lengths} H=2", flush=True)
+    w = wl.custom(lengths, H=2, dk=dk, dv=dk, name="pieces")
+    print(f"[case] pieces lengths={lengths} H=2 dk={dk}", flush=True)
     inp = wl.make_inputs(w, "cuda")
     st, out, pool, hdr = _run_with_ws(w, inp)
     assert st == 0
@@ -106,12 +107,16 @@ def test_many_pieces_against_oracle(lengths):
     _compare_all(w, inp, out, pool)
 
 
-def test_varlen_32k_plan_and_agreement():
-    """The benchmark workload: the three longest sequences are split; the balanced pass
-    agrees with the unbalanced one, and the library's pool path with the torch one."""
+@pytest.mark.parametrize("dk", [128, 64])
+def test_varlen_32k_plan_and_agreement(dk):
+    """The benchmark workload (and its lengths at dk = 64): the three longest sequences are
+    split; the balanced pass agrees with the unbalanced one, and the library's pool path
+    with the torch one."""
     from kda_testlib import run_fwd, rel_out, rel_fro, untouched_slots_identical
     w = wl.workload("varlen_32k")
-    print(f"[case] varlen_32k plan, lengths={w.lengths}", flush=True)
+    if dk != w.dk:
+        w = wl.custom(list(w.lengths), H=w.H, dk=dk, dv=dk, n_slots=w.n_slots, name="varlen_32k_dk64")
+    print(f"[case] varlen_32k plan dk={dk}, lengths={w.lengths}", flush=True)
     inp = wl.make_inputs(w, "cuda")
     st, out, pool, hdr = _run_with_ws(w, inp)
     assert st == 0
@@ -129,9 +134,10 @@ def test_varlen_32k_plan_and_agreement():
     assert torch.equal(pool.view(torch.int32), pool_l.view(torch.int32))
 
 
-def test_workspace_too_small_is_refused():
-    w = wl.custom((4096,), H=2, dk=128, dv=128, name="small_ws")
-    print("[case] too-small workspace", flush=True)
+@pytest.mark.parametrize("dk", [128, 64])
+def test_workspace_too_small_is_refused(dk):
+    w = wl.custom((4096,), H=2, dk=dk, dv=dk, name="small_ws")
+    print(f"[case] too-small workspace dk={dk}", flush=True)
     inp = wl.make_inputs(w, "cuda")
     d = _desc(w, inp)
     need = C.c_size_t(0)

@@ -119,20 +119,19 @@ def test_workspace_variant_error_paths(L):
     n = C.c_size_t(7)
     assert L.kda_chunk_fwd_workspace_size(None, C.byref(n)) == ENULL
     assert L.kda_chunk_fwd_workspace_size(C.byref(_desc()), None) == ENULL
-    # f32 and dk = 64 never use the load-balanced pass: no workspace, no device query
+    # f32 never uses the load-balanced pass: no workspace, no device query
     assert L.kda_chunk_fwd_workspace_size(C.byref(_desc(qkv_dtype=torch.float32, out_dtype=torch.float32,
                                                          dk=64, dv=64)), C.byref(n)) == OK
-    assert n.value == 0
-    assert L.kda_chunk_fwd_workspace_size(C.byref(_desc(dk=64, dv=64)), C.byref(n)) == OK
     assert n.value == 0
     # neither does the precise walk (bf16 with the original gate)
     assert L.kda_chunk_fwd_workspace_size(C.byref(_desc(gate_mode="original")), C.byref(n)) == OK
     assert n.value == 0
-    # bf16 dk = dv = 128 sizes for the current device (HIP error without one)
-    st = L.kda_chunk_fwd_workspace_size(C.byref(_desc()), C.byref(n))
-    assert st in (OK, 6)
-    if st == OK:
-        assert n.value >= 128 * 4 * 128 * 2
+    # bf16 with the safe gate sizes for the current device (HIP error without one)
+    for dk in (128, 64):
+        st = L.kda_chunk_fwd_workspace_size(C.byref(_desc(dk=dk, dv=dk)), C.byref(n))
+        assert st in (OK, 6)
+        if st == OK:
+            assert n.value >= 128 * 4 * dk * 2
 
 
 def _dec(L, d, **ptrs):
