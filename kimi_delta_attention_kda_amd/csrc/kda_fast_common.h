@@ -32,12 +32,8 @@ __device__ __forceinline__ int tile_row(int c) {
     return 16 * (2 * (c >> 5) + ((c >> 2) & 1)) + 4 * ((c >> 3) & 3) + (c & 3);
 }
 
-// A-operand fragment whose k slots follow the accumulator row order of two 16-row
+// fp16 A-operand fragment whose k slots follow the accumulator row order of two 16-row
 // tiles: slot s<4 -> column k0+4g+s, slot s>=4 -> column k0+16+4g+(s-4).
-__device__ __forceinline__ bf16x8 fragA_perm(const bf16_t *base, int pitch, int row, int k0, int g) {
-    const bf16_t *p = base + row * pitch + k0 + 4 * g;
-    return cat(*(const bf16x4 *)p, *(const bf16x4 *)(p + 16));
-}
 __device__ __forceinline__ f16x8 fragA_perm_h(const f16_t *base, int pitch, int row, int k0, int g) {
     const f16_t *p = base + row * pitch + k0 + 4 * g;
     return cath(*(const f16x4 *)p, *(const f16x4 *)(p + 16));

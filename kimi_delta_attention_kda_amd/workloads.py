@@ -17,6 +17,7 @@ Each named workload fixes shapes, dtypes, gate mode and sequence-length mix:
   varlen_32k       8 sequences, lengths in [1024, 8192] summing to 32768,
                    H=32, dk=dv=128, bf16 q/k/v/out, safe gate (lower bound -5),
                    64-slot pool, distinct random slots, states ~ N(0, 0.01^2)
+  varlen_32k_dk64  the same lengths and draws with dk=dv=64
   long_131k        1 x 131072 tokens, as varlen_32k, one zero slot
   segments_262k    1 x 262144 tokens as 16 segments of 16384, H=8, fp32,
                    original gate, initial state ~ N(0, 0.01^2)
@@ -87,6 +88,9 @@ def workload(name: str, seed: int = 0) -> Workload:
     if name == "varlen_32k":
         return Workload(name, _varlen_32k_lengths(rng), 32, 128, 128, "bf16", 1,
                         n_slots=64, state_sigma=0.01, seed=seed)
+    if name == "varlen_32k_dk64":
+        return Workload(name, _varlen_32k_lengths(rng), 32, 64, 64, "bf16", 1,
+                        n_slots=64, state_sigma=0.01, seed=seed)
     if name == "long_131k":
         return Workload(name, (131072,), 32, 128, 128, "bf16", 1, n_slots=1, seed=seed)
     if name == "segments_262k":
@@ -102,7 +106,7 @@ def workload(name: str, seed: int = 0) -> Workload:
     raise KeyError(name)
 
 
-NAMES = ("tiny_fp32", "varlen_32k", "long_131k", "segments_262k", "short_varlen_512", "decode_512")
+NAMES = ("tiny_fp32", "varlen_32k", "varlen_32k_dk64", "long_131k", "segments_262k", "short_varlen_512", "decode_512")
 
 
 def custom(lengths, H=2, dk=64, dv=64, dtype="bf16", gate_mode=1, n_slots=None,

@@ -113,9 +113,7 @@ def test_varlen_32k_plan_and_agreement(dk):
     split; the balanced pass agrees with the unbalanced one, and the library's pool path
     with the torch one."""
     from kda_testlib import run_fwd, rel_out, rel_fro, untouched_slots_identical
-    w = wl.workload("varlen_32k")
-    if dk != w.dk:
-        w = wl.custom(list(w.lengths), H=w.H, dk=dk, dv=dk, n_slots=w.n_slots, name="varlen_32k_dk64")
+    w = wl.workload("varlen_32k" if dk == 128 else "varlen_32k_dk64")
     print(f"[case] varlen_32k plan dk={dk}, lengths={w.lengths}", flush=True)
     inp = wl.make_inputs(w, "cuda")
     st, out, pool, hdr = _run_with_ws(w, inp)
