@@ -184,7 +184,9 @@ def main():
     fl = algorithmic_flops(w)
     fl_dense = dense_tile_flops(w)
     rec = {
-        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC if w.name == "varlen_32k" else
+        f"KDA prefill tokens/s, {w.name}: H={w.H} dk=dv={w.dk} {w.dtype}, {w.T} tokens",
+        "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
