@@ -19,7 +19,7 @@ bool key_heads_ok(const kda_desc *d) {
     return d->num_key_heads >= 0 && d->num_heads % key_heads(d) == 0;
 }
 
-// Common host-visible checks of the descriptor for the chunk walk.
+// Host-visible checks of the descriptor shared by the prefill and the segment summaries.
 kda_status check_desc(const kda_desc *d, bool summary) {
     if (!d) return KDA_ERR_NULL;
     if (d->total_tokens < 0 || d->num_heads <= 0 || d->dk <= 0 || d->dv <= 0) return KDA_ERR_SHAPE;

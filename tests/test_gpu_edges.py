@@ -81,15 +81,16 @@ def test_no_decay_long_against_oracle(dk):
     assert eo <= OUT_TOL_BF16 and es <= STATE_TOL
 
 
-def test_many_sequences_with_pieces():
+@pytest.mark.parametrize("dk", [128, 64])
+def test_many_sequences_with_pieces(dk):
     """5,000 short sequences and 4 long ones (H = 2): the planner's uncached paths, pieces
     of the long sequences, and the single queue of 10,000+ units."""
     from kda_testlib import compare_items, run_fwd, untouched_slots_identical, OUT_TOL_BF16, STATE_TOL
     rng = np.random.default_rng(7)
     short = rng.integers(1, 41, size=5000).tolist()
     lengths = [8000] + short[:2500] + [8000, 7000] + short[2500:] + [6000]
-    w = wl.custom(lengths, H=2, dk=128, dv=128, dtype="bf16", gate_mode=1, seed=12)
-    print(f"[case] many sequences B={w.B} T={w.T}", flush=True)
+    w = wl.custom(lengths, H=2, dk=dk, dv=dk, dtype="bf16", gate_mode=1, seed=12)
+    print(f"[case] many sequences B={w.B} T={w.T} dk={dk}", flush=True)
     inp = wl.make_inputs(w, "cuda")
     out, pool = run_fwd(w, inp)
     assert untouched_slots_identical(inp, pool)

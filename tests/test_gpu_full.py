@@ -30,10 +30,11 @@ def _check(w, inp, out, pool, items):
     assert es <= STATE_TOL
 
 
-def test_varlen_32k():
+@pytest.mark.parametrize("name", ["varlen_32k", "varlen_32k_dk64"])
+def test_varlen_32k(name):
     from kda_testlib import run_fwd, untouched_slots_identical
-    w = wl.workload("varlen_32k")
-    print(f"[case] varlen_32k lengths={w.lengths}", flush=True)
+    w = wl.workload(name)
+    print(f"[case] {name} lengths={w.lengths}", flush=True)
     inp = wl.make_inputs(w, "cuda")
     out, pool = run_fwd(w, inp)
     assert untouched_slots_identical(inp, pool)
