@@ -112,7 +112,7 @@ __device__ __forceinline__ void pair_of_wave(int w, int pp, int &bI, int &bJ) {
 // GQA: fewer key heads than value heads (a.Hk < a.H); q and k rows then have their own
 // stride and head.  The equal-heads instantiation keeps one set of row offsets.
 template <int DKT, int MODE, bool GQA>
-__global__ __launch_bounds__(Geo<DKT>::NT, 512 / Geo<DKT>::NT) void kda_fast_kernel(ChainArgs a) {
+__global__ __launch_bounds__(Geo<DKT>::NT, 1) void kda_fast_kernel(ChainArgs a) {
     using L = Lds<DKT, MODE>;
     using Gm = Geo<DKT>;
     constexpr int DK = Gm::DK, DV = Gm::DV, NW = Gm::NW, NT = Gm::NT, NCT = Gm::NCT, NKB = Gm::NKB;
