@@ -83,6 +83,18 @@ def decode_bytes(w) -> int:
     return w.B * (w.H * per_seq_head + w.HK * 2 * w.dk * e) + w.H * (w.dk + 1) * 4 + w.B * 4
 
 
+def segment_bytes(w) -> int:
+    """Compulsory HBM bytes of one summary-and-scan pass: k, v, the gate pre-activations and
+    beta read once; M and U written by the summaries and read once by the scan; the scan's
+    incoming and outgoing stacks and final state written, the initial state read."""
+    e = 2 if w.dtype == "bf16" else 4
+    n = w.segments
+    inputs = w.T * (w.HK * w.dk * e + w.H * (w.dv * e + w.dk * 4 + 4)) + w.H * (w.dk + 1) * 4 + (n + 1) * 4
+    maps = n * w.H * w.dk * (w.dk + w.dv) * 4
+    scan = 2 * n * w.H * w.dk * w.dv * 4 + 2 * w.H * w.dk * w.dv * 4
+    return inputs + 2 * maps + scan
+
+
 def cpu_baseline(w, inp, target_s=12.0):
     """The fp64 oracle on a bounded sample of the same workload, all host cores."""
     from oracle import build as obuild
@@ -130,7 +142,7 @@ def main():
 
     w = wl.workload(args.workload)
     if w.segments:
-        raise SystemExit("bench.py times kda_chunk_fwd and kda_decode workloads")
+        return run_segments(args, w)
     if w.name.startswith("decode"):
         return run_decode(args, w)
     dev = torch.device("cuda", 0)
@@ -281,6 +293,86 @@ def run_decode(args, w):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
                      "kernel": "kda_decode_kernel", "kernel_ms": round(kern_ms, 4),
+                     "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def run_segments(args, w):
+    """kda_segment_summary over the workload's equal segments, then kda_affine_exclusive_scan
+    of the maps from the initial state: one step of the per-segment pass of KDA Context
+    Parallelism on one GPU's share."""
+    import torch
+    import kimi_delta_attention_kda_amd as kda
+    from kimi_delta_attention_kda_amd import workloads as wl
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload={w.name} T={w.T} segments={w.segments} H={w.H} dk={w.dk} dv={w.dv} "
+          f"dtype={w.dtype}", file=sys.stderr, flush=True)
+    inp = wl.make_inputs(w, dev)
+    torch.cuda.synchronize()
+    gate = "safe" if w.gate_mode == 1 else "original"
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import build as obuild
+        from oracle import oracle as orc
+        obuild.build(force=False)
+        nth = orc.default_threads()
+        offs = inp["seg_offsets"].tolist()
+        # head 0, as many segments as fill the host threads once, scaled to every map
+        nseg = min(w.segments, nth)
+        its = [orc.item_from_inputs(inp, 0, 0, with_q=False, t0=offs[i], t1=offs[i + 1]) for i in range(nseg)]
+        t = time.perf_counter()
+        orc.segment_maps(its, w.dk, w.dv, w.gate_mode, w.lower_bound, w.beta_mode, nthreads=nth)
+        dt = time.perf_counter() - t
+        tok = offs[nseg] - offs[0]
+        cpu = {"value": tok / w.H / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+               "sample": f"segment maps of segments 0..{nseg - 1} for head 0 of {w.H} ({tok} tokens, "
+                         f"{dt:.1f} s), scaled to all heads; the scan is not included"}
+    n = w.segments
+    M = torch.empty((n, w.H, w.dk, w.dk), dtype=torch.float32, device=dev)
+    U = torch.empty((n, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    inc, outg = torch.empty_like(U), torch.empty_like(U)
+    fin = torch.empty_like(inp["S_init"])
+
+    def step():
+        kda.segment_summary(inp["k"], inp["v"], inp["raw_gate"], inp["beta_logits"], inp["a_log"],
+                            inp["dt_bias"], inp["seg_offsets"], gate_mode=gate, lower_bound=w.lower_bound,
+                            M=M, U=U)
+        kda.affine_exclusive_scan(M, U, inp["S_init"], inc, outg, fin)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    nbytes = segment_bytes(w)
+    achieved = nbytes / (kern_ms / 1e3) / 1e9
+    rec = {
+        "metric": f"KDA segment summaries + exclusive scan tokens/s, {w.name}: {w.segments} segments, "
+                  f"H={w.H} dk=dv={w.dk} {w.dtype}, {w.T} tokens",
+        "value": round(w.T / (ms_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "total_tokens": w.T, "segments": w.segments, "heads": w.H,
+                   "dk": w.dk, "dv": w.dv, "gate": gate},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
+                     "kernel": ("kda_fast_kernel" if w.dtype == "bf16" and w.gate_mode == 1 and w.lower_bound >= -5.3
+                                else "kda_chain_kernel") + " (summaries) + kda_affine_scan_kernel",
+                     "kernel_ms": round(kern_ms, 4),
                      "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
     }

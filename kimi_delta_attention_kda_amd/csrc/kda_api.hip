@@ -52,9 +52,6 @@ kda::ChainArgs base_args(const kda_desc *d) {
     return a;
 }
 
-// Value columns per workgroup of the precise chunk walk (kda_chain.hip).
-constexpr int CHAIN_SLICE = 64;
-
 // The fast kernel (kda_fast.hip) takes bf16 with the safe gate, whose bound keeps the
 // reciprocal of a 16-token block decay, e^{16 |bound|}, finite; everything else within
 // the contract runs the precise chunk walk.
@@ -227,7 +224,6 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
             e = kda::launch_fast(a, desc->dk, kda::MODE_FWD, (hipStream_t)stream);
         }
     } else {
-        a.n_slices = desc->dv / CHAIN_SLICE;
         e = kda::launch_chain(a, desc->dk, desc->qkv_dtype == KDA_BF16, kda::MODE_FWD, (hipStream_t)stream);
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -375,7 +371,6 @@ kda_status kda_segment_summary(const kda_desc *desc, const void *k, const void *
         a.n_slices = 2;
         e = kda::launch_fast(a, desc->dk, kda::MODE_SUMMARY, (hipStream_t)stream);
     } else {
-        a.n_slices = (desc->dk + desc->dv) / CHAIN_SLICE;
         e = kda::launch_chain(a, desc->dk, desc->qkv_dtype == KDA_BF16, kda::MODE_SUMMARY, (hipStream_t)stream);
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

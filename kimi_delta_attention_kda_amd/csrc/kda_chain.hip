@@ -1,8 +1,8 @@
 // kda_chain.hip -- chunk-parallel KDA prefill and segment summaries, precise variant, for
 // gfx950 (MI355X): fp32 or bf16 q/k/v, either gate form, dk = dv in {64, 128}.
 //
-// One workgroup (4 waves) owns one (sequence-or-segment, head, 64-column value slice) and
-// walks its 64-token chunks in order.  For each chunk it
+// One workgroup (4 waves) owns one (sequence-or-segment, head, column slice) and walks its
+// 64-token chunks in order.  For each chunk it
 //   1. computes the gate (log alpha = -exp(a_log) softplus(raw + dt_bias), optionally
 //      clamped from below), its running sum G from the chunk start, and beta;
 //   2. builds the decayed key-key scores A (strictly lower) and query-key scores P (lower)
@@ -52,7 +52,8 @@ struct Lds {
     static constexpr int VT = T + 64 * PF * 4;                   // V^T slice (f32)
     static constexpr int BETA = VT + (VG ? 0 : DVS * PF * 4);
     static constexpr int EG = BETA + 64 * 4;                     // e^{G_last} [DK]
-    static constexpr int X = EG + DK * 4;                        // inverse scratch [3][16][17]
+    static constexpr int GL = EG + DK * 4;                       // G_last [DK]
+    static constexpr int X = GL + DK * 4;                        // inverse scratch [3][16][17]
     static constexpr int BYTES = X + 3 * 16 * 17 * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget of one workgroup");
 };
@@ -218,6 +219,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 
     float *sBeta = (float *)(smem + L::BETA);
     float *sEG = (float *)(smem + L::EG);
+    float *sGL = (float *)(smem + L::GL);
     float *sX = (float *)(smem + L::X);
     float *sA = (float *)(smem + L::A);
     float *sK = (float *)(smem + L::K);
@@ -263,6 +265,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 }
             }
             sEG[c] = __expf(G);
+            sGL[c] = G;
         }
         if constexpr (!L::VG) {
 #pragma unroll
@@ -283,34 +286,85 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
         }
         __syncthreads();
 
-        // ---- decayed scores, elementwise over 4x4 tiles of the lower triangle
-        if (t < 136) {
-            int bi = 0;
-            while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
-            const int bj = t - bi * (bi + 1) / 2;
+        // ---- decayed scores, elementwise over the 4x4 tiles of the lower triangle.
+        // Threads 0..119 take the 120 tiles below the diagonal and threads 128..143 the 16
+        // diagonal tiles, so each wave's active lanes do one kind of tile; in the forward
+        // pass the remaining threads zero the upper tiles of P.
+        //  - Below the diagonal, e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with r the last
+        //    row of the column tile (j <= r < i).  G never increases along the chunk (every
+        //    log alpha is <= 0, and adding a non-positive number never rounds upwards), so
+        //    both factors are <= 1, and the column factor of j = r is 1: seven exponentials
+        //    per channel.
+        //  - On the diagonal, products of the one-step factors e^{G_x - G_(x-1)} <= 1:
+        //    three exponentials per channel.
+        const bool below = t < 120, ondiag = t >= 128 && t < 144;
+        if (below || ondiag) {
+            int bi, bj;
+            if (below) {
+                bi = 1;
+                while (bi * (bi + 1) / 2 <= t) ++bi;
+                bj = t - bi * (bi - 1) / 2;
+            } else {
+                bi = bj = t - 128;
+            }
             float accA[4][4], accP[4][4];
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
                 for (int y = 0; y < 4; ++y) { accA[x][y] = 0.f; accP[x][y] = 0.f; }
-            for (int c = 0; c < DK; ++c) {
-                float Ki[4], Qi[4], Gi[4], Kj[4], Gj[4];
+            // CPS channels per step, read as 8- or 16-byte rows (two in the dk = 128
+            // forward pass, whose registers allow no more)
+            constexpr int CPS = (FW && DK == 128) ? 2 : 4;
+            typedef float fv __attribute__((ext_vector_type(CPS)));
+            for (int c = 0; c < DK; c += CPS) {
+                fv Ki[4], Qi[4], Gi[4], Kj[4], Gj[4];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    Ki[x] = sK[(4 * bi + x) * PKF + c];
-                    Gi[x] = sG[(4 * bi + x) * PKF + c];
-                    Qi[x] = FW ? sQ[(4 * bi + x) * PKF + c] : 0.f;
-                    Kj[x] = sK[(4 * bj + x) * PKF + c];
-                    Gj[x] = sG[(4 * bj + x) * PKF + c];
+                    Ki[x] = *(const fv *)(sK + (4 * bi + x) * PKF + c);
+                    Gi[x] = *(const fv *)(sG + (4 * bi + x) * PKF + c);
+                    Qi[x] = FW ? *(const fv *)(sQ + (4 * bi + x) * PKF + c) : fv{};
+                    Kj[x] = *(const fv *)(sK + (4 * bj + x) * PKF + c);
+                    Gj[x] = *(const fv *)(sG + (4 * bj + x) * PKF + c);
                 }
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
+                for (int cc = 0; cc < CPS; ++cc) {
+                    float ri[4], cj[4][4];  // row factors; column factors times K_j, per row x
+                    if (below) {
+                        const float Gr = Gj[3][cc];
+                        float kej[4];
 #pragma unroll
-                    for (int y = 0; y < 4; ++y) {
-                        const float d = __expf(fminf(Gi[x] - Gj[y], 0.f)) * Kj[y];
-                        accA[x][y] += Ki[x] * d;
-                        accP[x][y] += Qi[x] * d;
+                        for (int y = 0; y < 3; ++y) kej[y] = __expf(Gr - Gj[y][cc]) * Kj[y][cc];
+                        kej[3] = Kj[3][cc];
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            ri[x] = __expf(Gi[x][cc] - Gr);
+#pragma unroll
+                            for (int y = 0; y < 4; ++y) cj[x][y] = kej[y];
+                        }
+                    } else {
+                        const float a1 = __expf(Gj[1][cc] - Gj[0][cc]), a2 = __expf(Gj[2][cc] - Gj[1][cc]),
+                                    a3 = __expf(Gj[3][cc] - Gj[2][cc]);
+                        const float D[4][4] = {{1.f, 0.f, 0.f, 0.f},
+                                               {a1, 1.f, 0.f, 0.f},
+                                               {a2 * a1, a2, 1.f, 0.f},
+                                               {a3 * (a2 * a1), a3 * a2, a3, 1.f}};
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            ri[x] = 1.f;
+#pragma unroll
+                            for (int y = 0; y < 4; ++y) cj[x][y] = D[x][y] * Kj[y][cc];
+                        }
                     }
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const float kx = Ki[x][cc] * ri[x], qx = Qi[x][cc] * ri[x];
+#pragma unroll
+                        for (int y = 0; y < 4; ++y) {
+                            accA[x][y] += kx * cj[x][y];
+                            accP[x][y] += qx * cj[x][y];
+                        }
+                    }
+                }
             }
 #pragma unroll
             for (int x = 0; x < 4; ++x)
@@ -320,9 +374,9 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                     sA[i * PF + j] = (j < i) ? sBeta[i] * accA[x][y] : 0.f;
                     if (FW) sP[i * PF + j] = (j <= i) ? accP[x][y] : 0.f;
                 }
-        } else if (FW && t < 136 + 120) {
-            // zero an upper 4x4 tile of P
-            int u = t - 136, bi = 0;
+        } else if (FW) {
+            // zero an upper 4x4 tile of P (threads 120..127 and 144..255: 120 tiles)
+            int u = t < 128 ? t - 120 : t - 136, bi = 0;
             while (u >= 15 - bi) { u -= 15 - bi; ++bi; }
             const int bj = bi + 1 + u;
 #pragma unroll
@@ -331,6 +385,17 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 for (int y = 0; y < 4; ++y) sP[(4 * bi + x) * PF + 4 * bj + y] = 0.f;
         }
         __syncthreads();
+        // The chain step's operands, formed once per element (the scores above were the last
+        // readers of K, Q and G as such): K e^{G} over K, Q e^{G} over Q, and
+        // K e^{G_last - G} over G.  The inverse below neither reads nor writes these arrays,
+        // and ends with a barrier.
+        for (int e = t; e < 64 * DK; e += NT) {
+            const int i = e / DK, c = e - i * DK;
+            const float G = sG[i * PKF + c], K = sK[i * PKF + c], eg = __expf(G);
+            sK[i * PKF + c] = K * eg;
+            if (FW) sQ[i * PKF + c] *= eg;
+            sG[i * PKF + c] = K * __expf(sGL[c] - G);
+        }
         invert_unit_lower<PF>(sA, sT, sX, t);
 
         // ---- chain step, all products split three ways
@@ -353,19 +418,14 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
             const int row = 16 * rt + li;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                float kv[8], gv[8], x[8];
-                load_perm_f32(sK, PKF, row, 32 * kb, g, kv);
-                load_perm_f32(sG, PKF, row, 32 * kb, g, gv);
-#pragma unroll
-                for (int s = 0; s < 8; ++s) x[s] = kv[s] * __expf(gv[s]);
+                float x[8];
+                load_perm_f32(sK, PKF, row, 32 * kb, g, x);  // K e^{G}
                 bf16x8 ah, alo;
                 split8(x, ah, alo);
 #pragma unroll
                 for (int m = 0; m < NVT; ++m) Y[m][rt] = mma3(Y[m][rt], ah, alo, Sh[m][kb], Sl[m][kb], true, true);
                 if (FW) {
-                    load_perm_f32(sQ, PKF, row, 32 * kb, g, kv);
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) x[s] = kv[s] * __expf(gv[s]);
+                    load_perm_f32(sQ, PKF, row, 32 * kb, g, x);  // Q e^{G}
                     split8(x, ah, alo);
 #pragma unroll
                     for (int m = 0; m < NVT; ++m)
@@ -444,15 +504,11 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 #pragma unroll
             for (int m = 0; m < NVT; ++m) S[m][ct] *= eg;
             const int c = 16 * ct + li;
-            const float glast = sG[63 * PKF + c];
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb) {
                 float x[8];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const int j = 32 * jb + perm_k(g, s);
-                    x[s] = sK[j * PKF + c] * __expf(glast - sG[j * PKF + c]);
-                }
+                for (int s = 0; s < 8; ++s) x[s] = sG[(32 * jb + perm_k(g, s)) * PKF + c];  // K e^{G_last - G}
                 bf16x8 ah, alo;
                 split8(x, ah, alo);
 #pragma unroll
@@ -485,7 +541,9 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 }
 
 template <int DK, int DVS, bool IN16, int MODE>
-static hipError_t launch_one(const ChainArgs &a, hipStream_t stream) {
+static hipError_t launch_one(const ChainArgs &a0, hipStream_t stream) {
+    ChainArgs a = a0;
+    a.n_slices = (MODE == MODE_FWD ? DK : 2 * DK) / DVS;  // value (or [M | U]) column slices
     const int n_units = a.n_items * a.H;
     const int groups = (n_units + 7) / 8;
     const dim3 grid(8 * a.n_slices * groups);
@@ -493,9 +551,12 @@ static hipError_t launch_one(const ChainArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Slice width dk: one workgroup per (sequence, head) in the forward pass and two (the
+// transition and the contribution columns) for summaries, so that the gate, the scores,
+// the inverse and the chain operands of a chunk are formed once per column block of dk.
 template <bool IN16, int MODE>
 static hipError_t launch_dk(const ChainArgs &a, int dk, hipStream_t stream) {
-    if (dk == 128) return launch_one<128, 64, IN16, MODE>(a, stream);
+    if (dk == 128) return launch_one<128, 128, IN16, MODE>(a, stream);
     if (dk == 64) return launch_one<64, 64, IN16, MODE>(a, stream);
     return hipErrorInvalidValue;
 }

@@ -69,9 +69,8 @@ struct ChainArgs {
     void *ws_W;              // [T][H][dv] bf16, W rows of the later pieces
 };
 
-// Precise chunk walk (kda_chain.hip): dk = dv in {64, 128}, 64 value columns per
-// workgroup (a.n_slices = dv / 64 for the forward pass, (dk + dv) / 64 for summaries);
-// bf16_in: q/k/v (and out) are bf16, else fp32.
+// Precise chunk walk (kda_chain.hip): dk = dv in {64, 128}; the launch sets a.n_slices
+// (column slices per item and head) itself.  bf16_in: q/k/v (and out) are bf16, else fp32.
 hipError_t launch_chain(const ChainArgs &a, int dk, bool bf16_in, int mode, hipStream_t stream);
 
 // bf16 inputs, dk = dv in {64, 128}, safe gate: dv/16-wave kernel, one workgroup per (item, head)

@@ -40,6 +40,15 @@ def test_grouped_key_heads_read_q_and_k_once_per_key_head():
     assert bench.algorithmic_bytes(w) == 128 * per_token + slots + 8 * 65 * 4 + 3 * 4 + 2 * 4
 
 
+def test_segment_pass_compulsory_bytes():
+    w = wl.workload("segments_262k")
+    assert (w.T, w.H, w.segments, w.dk, w.dv, w.dtype) == (262144, 8, 16, 128, 128, "f32")
+    inputs = 262144 * 8 * (128 * 4 + 128 * 4 + 128 * 4 + 4) + 8 * 129 * 4 + 17 * 4  # k v raw beta; gates; offsets
+    maps = 16 * 8 * 128 * 256 * 4                 # M and U, written then read by the scan
+    scan = 2 * 16 * 8 * 128 * 128 * 4 + 2 * 8 * 128 * 128 * 4   # incoming, outgoing; S_init, final
+    assert bench.segment_bytes(w) == inputs + 2 * maps + scan
+
+
 def test_decode_compulsory_bytes():
     w = wl.workload("decode_512")
     assert (w.B, w.T, w.H, w.dk, w.dv) == (512, 512, 32, 128, 128)
