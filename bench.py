@@ -29,7 +29,8 @@ METRIC = "KDA prefill tokens/s at H=32 dk=dv=128 bf16, 32K tokens; % MFMA peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILES = {"varlen_32k": os.path.join(ROOT, "profiles", "kda_chunk_fwd_varlen_32k_traffic.json"),
-                 "decode_512": os.path.join(ROOT, "profiles", "kda_decode_kernel_decode_512_traffic.json")}
+                 "decode_512": os.path.join(ROOT, "profiles", "kda_decode_kernel_decode_512_traffic.json"),
+                 "segments_262k": os.path.join(ROOT, "profiles", "kda_segment_pass_segments_262k_traffic.json")}
 
 
 def measured_traffic(w):
@@ -331,6 +332,8 @@ def run_segments(args, w):
         cpu = {"value": tok / w.H / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle",
                "sample": f"segment maps of segments 0..{nseg - 1} for head 0 of {w.H} ({tok} tokens, "
                          f"{dt:.1f} s), scaled to all heads; the scan is not included"}
+    if args.copy_calibration:
+        copy_calibration(dev)
     n = w.segments
     M = torch.empty((n, w.H, w.dk, w.dk), dtype=torch.float32, device=dev)
     U = torch.empty((n, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
