@@ -239,33 +239,50 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
             sBeta[t] = (t < n) ? beta_of(x, a.beta_mode) : 0.f;
         }
 
-        if (t < DK) {
-            const int c = t;
+        // gate, K and Q of the chunk: TPC threads per key channel, each taking RH consecutive
+        // rows, so every load of the chunk is issued at once; each part's running sum of
+        // log alpha is then offset by the totals of the parts before it (exchanged through
+        // the inverse's scratch, idle until the scores are done).  Adding the non-positive
+        // offsets keeps G non-increasing along the chunk.
+        {
+            // RB rows per batch of loads: all RH at once, or two batches in the dk = 128
+            // forward pass, whose registers allow no more
+            constexpr int TPC = NT / DK, RH = 64 / TPC, RB = (FW && DK == 128) ? RH / 2 : RH;
+            const int c = t % DK, part = t / DK;
             const float dtb = a.dt_bias[h * DK + c];
             float G = 0.f;
-            for (int i0 = 0; i0 < 64; i0 += 16) {
-                float rg[16], kk[16], qq[16];
+#pragma unroll 1
+            for (int r0 = 0; r0 < RH; r0 += RB) {
+                float rg[RB], kk[RB], qq[RB];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = i0 + r;
+                for (int r = 0; r < RB; ++r) {
+                    const int i = RH * part + r0 + r;
                     const int64_t row = t0 + min(i, n - 1);
-                    const int64_t base = (row * H + h) * DK + c;
+                    rg[r] = a.raw_gate[(row * H + h) * DK + c];
                     const int64_t kbase = (row * a.Hk + hk) * DK + c;
-                    rg[r] = a.raw_gate[base];
                     kk[r] = i < n ? ld_in<IN16>(a.k, kbase) : 0.f;
                     qq[r] = (FW && i < n) ? ld_in<IN16>(a.q, kbase) : 0.f;
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = i0 + r;
+                for (int r = 0; r < RB; ++r) {
+                    const int i = RH * part + r0 + r;
                     if (i < n) G += gate_log_alpha(rg[r], dtb, Ah, safe, lb);
-                    sG[i * PKF + c] = G;
+                    sG[i * PKF + c] = G;  // this part's own running sum for now
                     sK[i * PKF + c] = kk[r];
                     if (FW) sQ[i * PKF + c] = qq[r];
                 }
             }
-            sEG[c] = __expf(G);
-            sGL[c] = G;
+            sX[part * DK + c] = G;  // this part's total
+            __syncthreads();
+            float off = 0.f;
+            for (int p = 0; p < part; ++p) off += sX[p * DK + c];
+            if (part > 0)
+#pragma unroll
+                for (int r = 0; r < RH; ++r) sG[(RH * part + r) * PKF + c] += off;
+            if (part == TPC - 1) {
+                sEG[c] = __expf(off + G);
+                sGL[c] = off + G;
+            }
         }
         if constexpr (!L::VG) {
 #pragma unroll
