@@ -8,9 +8,9 @@
 //   2. builds the decayed key-key scores A (strictly lower) and query-key scores P (lower)
 //      elementwise, with exp of the non-positive differences G_i - G_j, so no factor
 //      e^{-G} is ever formed and any gate, however steep, stays finite;
-//   3. inverts the unit lower-triangular I + A in LDS (fp32);
+//   3. inverts the four 16x16 diagonal blocks of the unit lower-triangular I + A (fp32);
 //   4. with the fp32 state slice S [dk, 16-column tiles] resident in MFMA accumulators:
-//        U  = (I + A)^-1 Diag(beta) (V - (K o e^G) S)
+//        U  = (I + A)^-1 Diag(beta) (V - (K o e^G) S), by blocked forward substitution
 //        O  = scale ((Q o e^G) S + P U)
 //        S <- Diag(e^{G_last}) S + (K o e^{G_last - G})^T U
 //      with every MFMA operand split into bf16 hi + lo and the products summed three ways
@@ -53,8 +53,8 @@ struct Lds {
     static constexpr int BETA = VT + (VG ? 0 : DVS * PF * 4);
     static constexpr int EG = BETA + 64 * 4;                     // e^{G_last} [DK]
     static constexpr int GL = EG + DK * 4;                       // G_last [DK]
-    static constexpr int X = GL + DK * 4;                        // inverse scratch [3][16][17]
-    static constexpr int BYTES = X + 3 * 16 * 17 * 4;
+    static constexpr int X = GL + DK * 4;                        // load-phase part totals [256]
+    static constexpr int BYTES = X + 256 * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget of one workgroup");
 };
 
@@ -103,60 +103,36 @@ __device__ __forceinline__ f32x4 mma3(f32x4 acc, bf16x8 ah, bf16x8 al, bf16x8 bh
     return acc;
 }
 
-// Inverse of the unit lower-triangular 64x64 matrix I + A (A strictly lower, f32 in LDS,
-// pitch PF) into Tf (f32, pitch PF): 16x16 diagonal blocks by forward substitution, then
-// off-diagonal blocks by increasing distance: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ.
-template <int PF>
-__device__ __forceinline__ void invert_unit_lower(const float *sA, float *Tf, float *sX, int t) {
-    const int w = t >> 6, l = t & 63;
-    // zero the strictly upper blocks
-    for (int e = t; e < 6 * 256; e += NT) {
-        const int blk = e >> 8;  // (0,1),(0,2),(0,3),(1,2),(1,3),(2,3)
-        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        Tf[(16 * bi + ((e >> 4) & 15)) * PF + 16 * bj + (e & 15)] = 0.f;
+// (I + A_bb)^-1 of one 16x16 diagonal block, by right-looking substitution on the 64
+// lanes of a wave: column c = l/4 of the inverse lives on the four lanes of a quad, lane
+// quarter q holding rows 4q .. 4q+3 as acc = -x.  Step K takes acc_K from quad lane K/4
+// (a DPP quad broadcast) and folds x_K into the rows below K; the entries of A on and
+// above the diagonal are not read (the scores leave the upper tiles of a block unwritten).
+// Ab points at the block's first entry of A (fp32, row pitch PF).
+template <int PF, int K>
+__device__ __forceinline__ void diag_inv_step(float (&acc)[4], const float *Ab, int q) {
+    const float yk = __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc[K & 3]), (K >> 2) * 0x55, 0xF, 0xF, false));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float a = 4 * q + j > K ? Ab[(4 * q + j) * PF + K] : 0.f;
+        acc[j] = fmaf(-a, yk, acc[j]);
     }
-    if (l < 16) {
-        const int I = w, col = l;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.f : 0.f;
-#pragma unroll
-        for (int r = 1; r < 16; ++r) {
-            const float *arow = sA + (16 * I + r) * PF + 16 * I;
-            float s = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < r; ++kk) s += (kk >= col) ? arow[kk] * x[kk] : 0.f;
-            if (r > col) x[r] = -s;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tf[(16 * I + r) * PF + 16 * I + col] = x[r];
-    }
-    __syncthreads();
-    for (int d = 1; d < 4; ++d) {
-        const int nent = (4 - d) * 256;
-        for (int e = t; e < nent; e += NT) {
-            const int J = e >> 8, I = J + d, r = (e >> 4) & 15, c = e & 15;
-            float s = 0.f;
-            for (int K = J; K < I; ++K) {
-                const float *arow = sA + (16 * I + r) * PF + 16 * K;
-                const float *tcol = Tf + (16 * K) * PF + 16 * J + c;
-#pragma unroll
-                for (int kk = 0; kk < 16; ++kk) s += arow[kk] * tcol[kk * PF];
-            }
-            sX[(J * 16 + r) * 17 + c] = s;
-        }
-        __syncthreads();
-        for (int e = t; e < nent; e += NT) {
-            const int J = e >> 8, I = J + d, r = (e >> 4) & 15, c = e & 15;
-            const float *trow = Tf + (16 * I + r) * PF + 16 * I;
-            float s = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) s += (kk <= r) ? trow[kk] * sX[(J * 16 + kk) * 17 + c] : 0.f;
-            Tf[(16 * I + r) * PF + 16 * J + c] = -s;
-        }
-        __syncthreads();
-    }
+    if constexpr (K < 15) diag_inv_step<PF, K + 1>(acc, Ab, q);
+}
+
+// v_mfma_f32_16x16x16_bf16: D[16x16] += A[16x16] B[16x16]; lane (g, li): A slot s =
+// A[li][4g+s], B slot s = B[4g+s][li], D slot s = D[4g+s][li] (so an accumulator tile is
+// a B operand as it stands).
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0, 0);
+}
+// acc += A B with both operands split into bf16 hi + lo (lo*lo dropped)
+__device__ __forceinline__ f32x4 mma3x16(f32x4 acc, bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl) {
+    acc = mfma16(ah, bh, acc);
+    acc = mfma16(ah, bl, acc);
+    return mfma16(al, bh, acc);
 }
 
 template <int DK, int DVS, bool IN16, int MODE>
@@ -242,8 +218,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
         // gate, K and Q of the chunk: TPC threads per key channel, each taking RH consecutive
         // rows, so every load of the chunk is issued at once; each part's running sum of
         // log alpha is then offset by the totals of the parts before it (exchanged through
-        // the inverse's scratch, idle until the scores are done).  Adding the non-positive
-        // offsets keeps G non-increasing along the chunk.
+        // a small LDS array).  Adding the non-positive offsets keeps G non-increasing along
+        // the chunk.
         {
             // RB rows per batch of loads: all RH at once, or two batches in the dk = 128
             // forward pass, whose registers allow no more
@@ -413,7 +389,17 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
             if (FW) sQ[i * PKF + c] *= eg;
             sG[i * PKF + c] = K * __expf(sGL[c] - G);
         }
-        invert_unit_lower<PF>(sA, sT, sX, t);
+        {
+            // the four diagonal-block inverses of I + A, one per wave, into sT (fp32)
+            const int c = l >> 2, q = l & 3;
+            float acc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = (4 * q + j == c) ? -1.f : 0.f;
+            diag_inv_step<PF, 0>(acc, sA + 16 * w * PF + 16 * w, q);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sT[(16 * w + 4 * q + j) * PF + 16 * w + c] = -acc[j];
+        }
+        __syncthreads();
 
         // ---- chain step, all products split three ways
         bf16x8 Sh[NVT][NKB], Sl[NVT][NKB];
@@ -450,7 +436,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 }
             }
         }
-        bf16x4 Rh[NVT][4], Rl[NVT][4];
+        f32x4 R[NVT][4];
 #pragma unroll
         for (int m = 0; m < NVT; ++m) {
             const int vcol = 16 * (w * NVT + m) + li;
@@ -467,28 +453,32 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                     vv = *(const f32x4 *)(sVT + vcol * PF + 16 * rt + 4 * g);
                 }
                 const f32x4 bb = *(const f32x4 *)(sBeta + 16 * rt + 4 * g);
-                split4(bb * (vv - Y[m][rt]), Rh[m][rt], Rl[m][rt]);
+                R[m][rt] = bb * (vv - Y[m][rt]);
             }
         }
+        // (I + A) U = R by blocks: U_I = D_I (R_I - sum_{J<I} A_IJ U_J) with D_I the
+        // diagonal-block inverses; every product split three ways
         bf16x4 Uh[NVT][4], Ul[NVT][4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            f32x4 Uacc[NVT];
+        for (int bI = 0; bI < 4; ++bI) {
+            f32x4 acc[NVT];
 #pragma unroll
-            for (int m = 0; m < NVT; ++m) Uacc[m] = zero4();
+            for (int m = 0; m < NVT; ++m) acc[m] = R[m][bI];
 #pragma unroll
-            for (int jb = 0; jb <= (rt >> 1); ++jb) {
-                float x[8];
-                load_perm_f32(sT, PF, 16 * rt + li, 32 * jb, g, x);
-                bf16x8 ah, alo;
-                split8(x, ah, alo);
+            for (int bJ = 0; bJ < bI; ++bJ) {
+                bf16x4 ah, alo;
+                split4(-*(const f32x4 *)(sA + (16 * bI + li) * PF + 16 * bJ + 4 * g), ah, alo);
 #pragma unroll
-                for (int m = 0; m < NVT; ++m)
-                    Uacc[m] = mma3(Uacc[m], ah, alo, cat(Rh[m][2 * jb], Rh[m][2 * jb + 1]),
-                                   cat(Rl[m][2 * jb], Rl[m][2 * jb + 1]), true, true);
+                for (int m = 0; m < NVT; ++m) acc[m] = mma3x16(acc[m], ah, alo, Uh[m][bJ], Ul[m][bJ]);
             }
+            bf16x4 dh, dl;
+            split4(*(const f32x4 *)(sT + (16 * bI + li) * PF + 16 * bI + 4 * g), dh, dl);
 #pragma unroll
-            for (int m = 0; m < NVT; ++m) split4(Uacc[m], Uh[m][rt], Ul[m][rt]);
+            for (int m = 0; m < NVT; ++m) {
+                bf16x4 xh, xl;
+                split4(acc[m], xh, xl);
+                split4(mma3x16(zero4(), dh, dl, xh, xl), Uh[m][bI], Ul[m][bI]);
+            }
         }
         if (FW) {
 #pragma unroll
