@@ -374,7 +374,8 @@ def run_segments(args, w):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
                      "kernel": ("kda_fast_kernel" if w.dtype == "bf16" and w.gate_mode == 1 and w.lower_bound >= -5.3
-                                else "kda_chain_kernel") + " (summaries) + kda_affine_scan_kernel",
+                                else "kda_chain_kernel") + " (summaries) + "
+                               + ("kda_affine_scan_mfma" if w.dk in (64, 128) else "kda_affine_scan_kernel"),
                      "kernel_ms": round(kern_ms, 4),
                      "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": cpu,
