@@ -107,7 +107,7 @@ hipMemPool_t device_pool(int dev) {
 
 bool planned_applies(const kda_desc *d) { return use_fast(d) && d->batch > 0 && d->total_tokens > 0; }
 
-// chunk kernel of the bf16 dk = dv = 128 forward pass
+// chunk kernel of the bf16 forward pass (dk = dv in {64, 128})
 const kda::FwdKernel &fwd_kernel() { return kda::FWD64; }
 
 kda_status workspace_bytes_for(const kda_desc *d, size_t *bytes, kda::PlanLayout *lay, int *n_cu) {

@@ -1,4 +1,4 @@
-// kda_fast_common.h -- device helpers of the dk = dv = 128 chunk kernel (kda_fast.hip).
+// kda_fast_common.h -- device helpers of the bf16 chunk kernel (kda_fast.hip).
 #pragma once
 
 #include "kda_common.h"
