@@ -46,6 +46,19 @@ def measured_traffic(w):
     return None
 
 
+def measured_utilization(w):
+    """MFMA- and VALU-busy fractions of the chunk kernel from the counter summary of this
+    workload, while the kernel sources still hash to the measured version; else None."""
+    f = os.path.join(ROOT, "profiles", f"kda_fast_kernel_{w.name}_utilization.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        u = json.load(fh)
+    if u.get("kernel_source_sha") == kernel_source_sha() and u.get("workload") == w.name:
+        return {"mfma_busy": u.get("mfma_busy"), "valu_busy": u.get("valu_busy"), "from": u.get("source")}
+    return None
+
+
 def kernel_source_sha() -> str:
     d = os.path.join(ROOT, "kimi_delta_attention_kda_amd", "csrc")
     h = hashlib.sha256()
@@ -213,6 +226,7 @@ def main():
         "mfma": {"algorithmic_tflops": round(fl / (kern_ms / 1e3) / 1e12, 2),
                  "frac_of_bf16_peak": round(fl / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "dense_tile_frac_of_bf16_peak": round(fl_dense / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "profiled_busy": measured_utilization(w),
                  "flops_per_launch_algorithmic": fl},
         "cpu_baseline": cpu,
     }
