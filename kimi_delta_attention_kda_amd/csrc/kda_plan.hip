@@ -479,10 +479,18 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         for (int i = t; i < n_piece; i += 256) spc[i] = p.piece[i];
     __syncthreads();
     auto piece_at = [&](int i) { return staged ? spc[i] : p.piece[i]; };
-    int cur = -1;
-    // groups of FIX_TASKS consecutive tasks, strided over the grid
-    for (int64_t grp = blockIdx.x; grp * FIX_TASKS < n_tasks; grp += gridDim.x)
-    for (int64_t task = grp * FIX_TASKS; task < min(n_tasks, (grp + 1) * FIX_TASKS); ++task) {
+    // The k-th task of this workgroup: groups of FIX_TASKS consecutive tasks, strided over
+    // the grid; -1 past the last (every later k is past it too).
+    auto task_of = [&](int64_t k) -> int64_t {
+        const int64_t grp = blockIdx.x + (k / FIX_TASKS) * gridDim.x;
+        const int64_t task = grp * FIX_TASKS + k % FIX_TASKS;
+        return task < min(n_tasks, (grp + 1) * FIX_TASKS) ? task : -1;
+    };
+    struct Task {
+        int key, t0, n, h;
+        int64_t rowh;  // this lane's row (token, head); rows past the chunk's end repeat its last
+    };
+    auto decode = [&](int64_t task) {
         int lo = 0, hi = n_piece - 1;  // last piece whose task range starts at or before task
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -492,32 +500,52 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         const int4 pc = piece_at(lo);
         const int len = pc.z;
         const int64_t rem = task - (int64_t)H * pc.w;
-        const int h = (int)(rem / len), c = (int)(rem - (int64_t)h * len);
-        const int key = lo * H + h;
-        const int t0 = pc.x + p.cs * c;
-        const int n = min(p.cs, pc.y - t0);
-        // this wave's loads first; rows past the chunk's end repeat its last row and are
-        // not stored (a wave past the end of a short chunk only joins the barriers)
-        const int64_t rowh = (int64_t)(t0 + min(16 * w + li, n - 1)) * H + h;
-        bf16x8 bw[DK / 32];
-        bf16x4 ov[DV / 16];
+        Task k;
+        k.h = (int)(rem / len);
+        const int c = (int)(rem - (int64_t)k.h * len);
+        k.key = lo * H + k.h;
+        k.t0 = pc.x + p.cs * c;
+        k.n = min(p.cs, pc.y - k.t0);
+        k.rowh = (int64_t)(k.t0 + min(16 * w + li, k.n - 1)) * H + k.h;
+        return k;
+    };
+    bf16x8 bw[DK / 32];
+    bf16x4 ov[DV / 16];
+    auto load = [&](const Task &k, bf16x8 (&b)[DK / 32], bf16x4 (&o)[DV / 16]) {
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) bw[kb] = *(const bf16x8 *)(p.W + rowh * DK + 32 * kb + 8 * g);
+        for (int kb = 0; kb < DK / 32; ++kb) b[kb] = *(const bf16x8 *)(p.W + k.rowh * DK + 32 * kb + 8 * g);
 #pragma unroll
-        for (int ct = 0; ct < DV / 16; ++ct) ov[ct] = *(const bf16x4 *)(p.out + rowh * DV + 16 * ct + 4 * g);
-        if (key != cur) {  // uniform over the workgroup
+        for (int ct = 0; ct < DV / 16; ++ct) o[ct] = *(const bf16x4 *)(p.out + k.rowh * DV + 16 * ct + 4 * g);
+    };
+    int cur = -1;
+    int64_t tk = task_of(0);  // valid: this workgroup has at least one task
+    Task tc = decode(tk);
+    load(tc, bw, ov);
+    for (int64_t k = 0; tk >= 0; ++k) {
+        // the next task's rows are in flight while this one is corrected (tasks cover
+        // disjoint rows, so the early reads of out see no store of this workgroup)
+        const int64_t tn = task_of(k + 1);
+        Task nt = tc;
+        bf16x8 bwn[DK / 32];
+        bf16x4 ovn[DV / 16];
+        if (tn >= 0) {  // uniform over the workgroup
+            nt = decode(tn);
+            load(nt, bwn, ovn);
+        }
+        if (tc.key != cur) {  // uniform over the workgroup
             __syncthreads();  // every wave is done with the previous X^T
-            const bf16_t *xt = p.XT + (int64_t)key * DV * DK;
+            const bf16_t *xt = p.XT + (int64_t)tc.key * DV * DK;
 #pragma unroll
             for (int i = 0; i < DV * DK / (8 * 256); ++i) {
                 const int e = 8 * (t + 256 * i), r = e / DK, cc = e - r * DK;
                 *(bf16x8 *)(sxt + r * FIX_XP + cc) = *(const bf16x8 *)(xt + e);
             }
             __syncthreads();
-            cur = key;
+            cur = tc.key;
         }
-        const bool store = 16 * w + li < n;
-        bf16_t *o = p.out + ((int64_t)(t0 + 16 * w + li) * H + h) * DV + 4 * g;
+        // a wave past the end of a short chunk only joins the barriers
+        const bool store = 16 * w + li < tc.n;
+        bf16_t *o = p.out + ((int64_t)(tc.t0 + 16 * w + li) * H + tc.h) * DV + 4 * g;
 #pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct) {
             f32x4 acc = f4(ov[ct]);
@@ -526,6 +554,12 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
                 acc = mfma(*(const bf16x8 *)(sxt + (16 * ct + li) * FIX_XP + 32 * kb + 8 * g), bw[kb], acc);
             if (store) *(bf16x4 *)(o + 16 * ct) = bf4(acc);
         }
+        tk = tn;
+        tc = nt;
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) bw[kb] = bwn[kb];
+#pragma unroll
+        for (int ct = 0; ct < DV / 16; ++ct) ov[ct] = ovn[ct];
     }
 }
 
