@@ -144,3 +144,33 @@ def test_workspace_too_small_is_refused(dk):
     st, _, pool, _ = _run_with_ws(w, inp, nbytes=need.value - 1)
     assert st == 2  # KDA_ERR_SHAPE, nothing launched
     assert torch.equal(pool.view(torch.int32), inp["state_pool"].view(torch.int32))
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_random_mixes_plan_and_agreement(dk):
+    """Seeded random batches (1 to 40 sequences of 1 to 20,000 tokens, 1 to 3 heads, some empty):
+    the device plan equals the host rule, and the balanced pass agrees with the unbalanced one
+    (outputs within the bf16 bound, states within the state bound)."""
+    from kda_testlib import run_fwd, rel_out, rel_fro, untouched_slots_identical, OUT_TOL_BF16, STATE_TOL
+    rng = np.random.default_rng(100 + dk)
+    for trial in range(6):
+        B = int(rng.integers(1, 41))
+        lengths = rng.integers(1, 20001, size=B)
+        lengths[rng.random(B) < 0.1] = 0
+        H = int(rng.integers(1, 4))
+        w = wl.custom(lengths.tolist(), H=H, dk=dk, dv=dk, seed=200 + trial, name="mix")
+        if w.T == 0:
+            continue
+        print(f"[case] random mix {trial}: dk={dk} B={B} H={H} T={w.T}", flush=True)
+        inp = wl.make_inputs(w, "cuda")
+        st, out, pool, hdr = _run_with_ws(w, inp)
+        assert st == 0
+        _check_plan(w, hdr)
+        assert untouched_slots_identical(inp, pool)
+        out_n, pool_n = run_fwd(w, inp, workspace="none")
+        for b in range(w.B):
+            a, e = inp["cu"][b], inp["cu"][b + 1]
+            s = inp["indices"][b]
+            if e > a:
+                assert rel_out(wl.as_f64(out[a:e]), wl.as_f64(out_n[a:e])) <= OUT_TOL_BF16
+            assert rel_fro(wl.as_f64(pool[s]), wl.as_f64(pool_n[s])) <= STATE_TOL
