@@ -280,49 +280,44 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
         __syncthreads();
 
         // ---- decayed scores, elementwise over the 4x4 tiles of the lower triangle.
-        // Threads 0..119 take the 120 tiles below the diagonal and threads 128..143 the 16
-        // diagonal tiles, so each wave's active lanes do one kind of tile; in the forward
-        // pass the remaining threads zero the upper tiles of P.
         //  - Below the diagonal, e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with r the last
         //    row of the column tile (j <= r < i).  G never increases along the chunk (every
         //    log alpha is <= 0, and adding a non-positive number never rounds upwards), so
         //    both factors are <= 1, and the column factor of j = r is 1: seven exponentials
-        //    per channel.
-        //  - On the diagonal, products of the one-step factors e^{G_x - G_(x-1)} <= 1:
-        //    three exponentials per channel.
-        const bool below = t < 120, ondiag = t >= 128 && t < 144;
-        if (below || ondiag) {
-            int bi, bj;
-            if (below) {
-                bi = 1;
-                while (bi * (bi + 1) / 2 <= t) ++bi;
-                bj = t - bi * (bi - 1) / 2;
-            } else {
-                bi = bj = t - 128;
-            }
+        //    per channel.  Each of the 120 tiles is split over two threads by key-channel
+        //    halves (threads u and u + 128), which keeps all four waves busy; the second
+        //    half's sums pass through the tile's own entries of A and P.
+        //  - On the diagonal, products of the one-step factors e^{G_x - G_(x-1)} <= 1 (three
+        //    exponentials per channel), on wave 3 once its half-tiles are done: a quad of
+        //    lanes per tile, one channel quarter each, summed with DPP.
+        {
+            // CPS channels per step, read as 8- or 16-byte rows (two in the dk = 128 forward
+            // pass, whose registers allow no more)
+            constexpr int CPS = (FW && DK == 128) ? 2 : 4;
+            typedef float fv __attribute__((ext_vector_type(CPS)));
+            const int u = t & 127, half = t >> 7;
+            const bool below = u < 120;
+            int bi = 1, bj = 0;
             float accA[4][4], accP[4][4];
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
                 for (int y = 0; y < 4; ++y) { accA[x][y] = 0.f; accP[x][y] = 0.f; }
-            // CPS channels per step, read as 8- or 16-byte rows (two in the dk = 128
-            // forward pass, whose registers allow no more)
-            constexpr int CPS = (FW && DK == 128) ? 2 : 4;
-            typedef float fv __attribute__((ext_vector_type(CPS)));
-            for (int c = 0; c < DK; c += CPS) {
-                fv Ki[4], Qi[4], Gi[4], Kj[4], Gj[4];
+            if (below) {
+                while (bi * (bi + 1) / 2 <= u) ++bi;
+                bj = u - bi * (bi - 1) / 2;
+                for (int c = half * (DK / 2); c < (half + 1) * (DK / 2); c += CPS) {
+                    fv Ki[4], Qi[4], Gi[4], Kj[4], Gj[4];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    Ki[x] = *(const fv *)(sK + (4 * bi + x) * PKF + c);
-                    Gi[x] = *(const fv *)(sG + (4 * bi + x) * PKF + c);
-                    Qi[x] = FW ? *(const fv *)(sQ + (4 * bi + x) * PKF + c) : fv{};
-                    Kj[x] = *(const fv *)(sK + (4 * bj + x) * PKF + c);
-                    Gj[x] = *(const fv *)(sG + (4 * bj + x) * PKF + c);
-                }
+                    for (int x = 0; x < 4; ++x) {
+                        Ki[x] = *(const fv *)(sK + (4 * bi + x) * PKF + c);
+                        Gi[x] = *(const fv *)(sG + (4 * bi + x) * PKF + c);
+                        Qi[x] = FW ? *(const fv *)(sQ + (4 * bi + x) * PKF + c) : fv{};
+                        Kj[x] = *(const fv *)(sK + (4 * bj + x) * PKF + c);
+                        Gj[x] = *(const fv *)(sG + (4 * bj + x) * PKF + c);
+                    }
 #pragma unroll
-                for (int cc = 0; cc < CPS; ++cc) {
-                    float ri[4], cj[4][4];  // row factors; column factors times K_j, per row x
-                    if (below) {
+                    for (int cc = 0; cc < CPS; ++cc) {
                         const float Gr = Gj[3][cc];
                         float kej[4];
 #pragma unroll
@@ -330,52 +325,95 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                         kej[3] = Kj[3][cc];
 #pragma unroll
                         for (int x = 0; x < 4; ++x) {
-                            ri[x] = __expf(Gi[x][cc] - Gr);
+                            const float ri = __expf(Gi[x][cc] - Gr);
+                            const float kx = Ki[x][cc] * ri, qx = Qi[x][cc] * ri;
 #pragma unroll
-                            for (int y = 0; y < 4; ++y) cj[x][y] = kej[y];
+                            for (int y = 0; y < 4; ++y) {
+                                accA[x][y] += kx * kej[y];
+                                accP[x][y] += qx * kej[y];
+                            }
                         }
-                    } else {
-                        const float a1 = __expf(Gj[1][cc] - Gj[0][cc]), a2 = __expf(Gj[2][cc] - Gj[1][cc]),
-                                    a3 = __expf(Gj[3][cc] - Gj[2][cc]);
+                    }
+                }
+                if (half == 1)  // the second half's sums, picked up below
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+#pragma unroll
+                        for (int y = 0; y < 4; ++y) {
+                            const int i = 4 * bi + x, j = 4 * bj + y;
+                            sA[i * PF + j] = accA[x][y];
+                            if (FW) sP[i * PF + j] = accP[x][y];
+                        }
+            }
+            __syncthreads();
+            if (below && half == 0)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) {
+                        const int i = 4 * bi + x, j = 4 * bj + y;
+                        sA[i * PF + j] = sBeta[i] * (accA[x][y] + sA[i * PF + j]);
+                        if (FW) sP[i * PF + j] = accP[x][y] + sP[i * PF + j];
+                    }
+            if (w == 3) {
+                const int b = l >> 2, qc = l & 3;  // tile (b, b), channel quarter qc
+                float dA[4][4], dP[4][4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) { dA[x][y] = 0.f; dP[x][y] = 0.f; }
+                for (int c = qc * (DK / 4); c < (qc + 1) * (DK / 4); c += CPS) {
+                    fv K4[4], Q4[4], G4[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        K4[x] = *(const fv *)(sK + (4 * b + x) * PKF + c);
+                        G4[x] = *(const fv *)(sG + (4 * b + x) * PKF + c);
+                        Q4[x] = FW ? *(const fv *)(sQ + (4 * b + x) * PKF + c) : fv{};
+                    }
+#pragma unroll
+                    for (int cc = 0; cc < CPS; ++cc) {
+                        const float a1 = __expf(G4[1][cc] - G4[0][cc]), a2 = __expf(G4[2][cc] - G4[1][cc]),
+                                    a3 = __expf(G4[3][cc] - G4[2][cc]);
                         const float D[4][4] = {{1.f, 0.f, 0.f, 0.f},
                                                {a1, 1.f, 0.f, 0.f},
                                                {a2 * a1, a2, 1.f, 0.f},
                                                {a3 * (a2 * a1), a3 * a2, a3, 1.f}};
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            ri[x] = 1.f;
+                        for (int x = 0; x < 4; ++x)
 #pragma unroll
-                            for (int y = 0; y < 4; ++y) cj[x][y] = D[x][y] * Kj[y][cc];
-                        }
+                            for (int y = 0; y <= x; ++y) {
+                                const float d = D[x][y] * K4[y][cc];
+                                dA[x][y] += K4[x][cc] * d;
+                                dP[x][y] += Q4[x][cc] * d;
+                            }
                     }
+                }
+                auto quad_sum = [](float v) {
+                    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+                    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+                };
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const float kx = Ki[x][cc] * ri[x], qx = Qi[x][cc] * ri[x];
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int y = 0; y <= x; ++y) {
+                        dA[x][y] = quad_sum(dA[x][y]);
+                        if (FW) dP[x][y] = quad_sum(dP[x][y]);
+                    }
+                if (qc == 0)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
 #pragma unroll
                         for (int y = 0; y < 4; ++y) {
-                            accA[x][y] += kx * cj[x][y];
-                            accP[x][y] += qx * cj[x][y];
+                            const int i = 4 * b + x, j = 4 * b + y;
+                            sA[i * PF + j] = (y < x) ? sBeta[i] * dA[x][y] : 0.f;
+                            if (FW) sP[i * PF + j] = (y <= x) ? dP[x][y] : 0.f;
                         }
-                    }
-                }
             }
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    const int i = 4 * bi + x, j = 4 * bj + y;
-                    sA[i * PF + j] = (j < i) ? sBeta[i] * accA[x][y] : 0.f;
-                    if (FW) sP[i * PF + j] = (j <= i) ? accP[x][y] : 0.f;
+            if (FW)  // the strictly upper tiles of P are zero
+                for (int e = t; e < 64 * 64; e += NT) {
+                    const int i = e >> 6, j = e & 63;
+                    if ((j >> 2) > (i >> 2)) sP[i * PF + j] = 0.f;
                 }
-        } else if (FW) {
-            // zero an upper 4x4 tile of P (threads 120..127 and 144..255: 120 tiles)
-            int u = t < 128 ? t - 120 : t - 136, bi = 0;
-            while (u >= 15 - bi) { u -= 15 - bi; ++bi; }
-            const int bj = bi + 1 + u;
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int y = 0; y < 4; ++y) sP[(4 * bi + x) * PF + 4 * bj + y] = 0.f;
         }
         __syncthreads();
         // The chain step's operands, formed once per element (the scores above were the last
