@@ -48,7 +48,7 @@ struct Lds {
     static constexpr int G = Q + (FW ? 64 * PKF * 4 : 0);        // G (f32)
     static constexpr int A = G + 64 * PKF * 4;                   // A (f32)
     static constexpr int P = A + 64 * PF * 4;                    // P (f32, FWD)
-    static constexpr int T = P + (FW ? 64 * PF * 4 : 0);         // (I + A)^-1 (f32)
+    static constexpr int T = P + (FW ? 64 * PF * 4 : 0);         // inverses of the diagonal blocks of I + A (f32)
     static constexpr int VT = T + 64 * PF * 4;                   // V^T slice (f32)
     static constexpr int BETA = VT + (VG ? 0 : DVS * PF * 4);
     static constexpr int EG = BETA + 64 * 4;                     // e^{G_last} [DK]
