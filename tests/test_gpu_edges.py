@@ -46,12 +46,16 @@ def _extreme_inputs(w):
     return inp
 
 
-@pytest.mark.parametrize("dtype,dk,gate", [("bf16", 128, 1), ("bf16", 64, 1), ("f32", 64, 0), ("f32", 64, 1)])
-def test_extreme_gates_against_oracle(dtype, dk, gate):
+@pytest.mark.parametrize("dtype,dk,gate,lb", [("bf16", 128, 1, -5.0), ("bf16", 64, 1, -5.0), ("bf16", 128, 1, -5.3),
+                                              ("f32", 64, 0, -5.0), ("f32", 64, 1, -5.0)])
+def test_extreme_gates_against_oracle(dtype, dk, gate, lb):
+    """bound -5.3 is the edge of the fast kernel's range: a 16-token block at the floor
+    decays by e^-84.8, whose reciprocal is near the top of the fp32 and bf16 range."""
     from kda_testlib import compare_items, run_fwd, untouched_slots_identical
     from kda_testlib import OUT_TOL_BF16, OUT_TOL_F32, STATE_TOL
-    w = wl.custom([200, 200, 333, 150, 150], H=2, dk=dk, dv=dk, dtype=dtype, gate_mode=gate, seed=11)
-    print(f"[case] extreme gates {dtype} dk={dk} gate_mode={gate}", flush=True)
+    w = wl.custom([200, 200, 333, 150, 150], H=2, dk=dk, dv=dk, dtype=dtype, gate_mode=gate, seed=11,
+                  lower_bound=lb)
+    print(f"[case] extreme gates {dtype} dk={dk} gate_mode={gate} bound={lb}", flush=True)
     inp = _extreme_inputs(w)
     out, pool = run_fwd(w, inp)
     assert torch.isfinite(out.float()).all()
