@@ -45,8 +45,9 @@ struct Lds {
     static constexpr int PKF = DK + 4;   // fp32 pitch, [64][DK]
     static constexpr int K = 0;                                  // K (f32)
     static constexpr int Q = K + 64 * PKF * 4;                   // Q (f32, FWD)
-    static constexpr int G = Q + (FW ? 64 * PKF * 4 : 0);        // G (f32)
-    static constexpr int A = G + 64 * PKF * 4;                   // A (f32)
+    static constexpr int G = Q + (FW ? 64 * PKF * 4 : 0);        // G [64][DK], then (K e^{G_last-G})^T [DK][64] (f32)
+    static constexpr int GB = (64 * PKF > DK * PF ? 64 * PKF : DK * PF) * 4;
+    static constexpr int A = G + GB;                             // A (f32)
     static constexpr int P = A + 64 * PF * 4;                    // P (f32, FWD)
     static constexpr int T = P + (FW ? 64 * PF * 4 : 0);         // inverses of the diagonal blocks of I + A (f32)
     static constexpr int VT = T + 64 * PF * 4;                   // V^T slice (f32)
@@ -91,8 +92,6 @@ __device__ __forceinline__ void load_perm_f32(const float *base, int pitch, int 
     x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
     x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
-
-__device__ __forceinline__ int perm_k(int g, int s) { return s < 4 ? 4 * g + s : 16 + 4 * g + (s - 4); }
 
 // acc += A B with optional hi/lo splits of either operand (lo*lo dropped).
 __device__ __forceinline__ f32x4 mma3(f32x4 acc, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl,
@@ -279,34 +278,44 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
         }
         __syncthreads();
 
-        // ---- decayed scores, elementwise over the 4x4 tiles of the lower triangle.
-        //  - Below the diagonal, e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with r the last
-        //    row of the column tile (j <= r < i).  G never increases along the chunk (every
-        //    log alpha is <= 0, and adding a non-positive number never rounds upwards), so
-        //    both factors are <= 1, and the column factor of j = r is 1: seven exponentials
-        //    per channel.  Each of the 120 tiles is split over two threads by key-channel
-        //    halves (threads u and u + 128), which keeps all four waves busy; the second
-        //    half's sums pass through the tile's own entries of A and P.
-        //  - On the diagonal, products of the one-step factors e^{G_x - G_(x-1)} <= 1 (three
-        //    exponentials per channel), on wave 3 once its half-tiles are done: a quad of
-        //    lanes per tile, one channel quarter each, summed with DPP.
+        // ---- decayed scores A (beta folded in) and P.
+        //  - Off-diagonal 16x16 blocks (row block I > column block J) as MFMA products:
+        //    e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with r = 16 I - 1, the row just above
+        //    the row block, so A_IJ = (K_I o e^{G_I - G_r}) (K_J o e^{G_r - G_J})^T and both
+        //    operands are bounded by |K| (G never increases along the chunk: every log alpha
+        //    is <= 0, and adding a non-positive number never rounds upwards).  Wave 0 takes
+        //    (1,0); wave 1 (2,1) and (2,0); wave 2 (3,2) and (3,1); wave 3 (3,0): the row
+        //    operand is formed once per wave and each column operand once per block.
+        //  - Inside the diagonal 16-blocks, elementwise over 4x4 tiles.  Below the diagonal of
+        //    4x4 tiles, through the last row r of the column tile (seven exponentials per
+        //    channel, both factors <= 1): 24 tiles on waves 0-2, eight lanes per tile with one
+        //    channel part each, summed with DPP.  On the diagonal, products of the one-step
+        //    factors e^{G_x - G_(x-1)} <= 1 (three exponentials per channel), on wave 3: a quad
+        //    of lanes per tile, one channel quarter each.
         {
             // CPS channels per step, read as 8- or 16-byte rows (two in the dk = 128 forward
             // pass, whose registers allow no more)
             constexpr int CPS = (FW && DK == 128) ? 2 : 4;
             typedef float fv __attribute__((ext_vector_type(CPS)));
-            const int u = t & 127, half = t >> 7;
-            const bool below = u < 120;
-            int bi = 1, bj = 0;
-            float accA[4][4], accP[4][4];
+            auto dpp_add = [](float v, int ctrl_sel) {
+                const int x = __builtin_bit_cast(int, v);
+                const int y = ctrl_sel == 0 ? __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false)    // lane ^ 1
+                            : ctrl_sel == 1 ? __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false)    // lane ^ 2
+                                            : __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // 7 - lane in 8
+                return v + __builtin_bit_cast(float, y);
+            };
+            if (w < 3) {
+                constexpr int CPP = DK / 8;  // channels per part
+                const int u = t >> 3, part = t & 7;
+                const int db = u / 6, lu = u - 6 * db;
+                const int bi4 = lu < 1 ? 1 : (lu < 3 ? 2 : 3), bj4 = lu - bi4 * (bi4 - 1) / 2;
+                const int bi = 4 * db + bi4, bj = 4 * db + bj4;
+                float accA[4][4], accP[4][4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+                for (int x = 0; x < 4; ++x)
 #pragma unroll
-                for (int y = 0; y < 4; ++y) { accA[x][y] = 0.f; accP[x][y] = 0.f; }
-            if (below) {
-                while (bi * (bi + 1) / 2 <= u) ++bi;
-                bj = u - bi * (bi - 1) / 2;
-                for (int c = half * (DK / 2); c < (half + 1) * (DK / 2); c += CPS) {
+                    for (int y = 0; y < 4; ++y) { accA[x][y] = 0.f; accP[x][y] = 0.f; }
+                for (int c = part * CPP; c < (part + 1) * CPP; c += CPS) {
                     fv Ki[4], Qi[4], Gi[4], Kj[4], Gj[4];
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
@@ -335,27 +344,25 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                         }
                     }
                 }
-                if (half == 1)  // the second half's sums, picked up below
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int y = 0; y < 4; ++y)
+#pragma unroll
+                        for (int st = 0; st < 3; ++st) {
+                            accA[x][y] = dpp_add(accA[x][y], st);
+                            if (FW) accP[x][y] = dpp_add(accP[x][y], st);
+                        }
+                if (part == 0)
 #pragma unroll
                     for (int x = 0; x < 4; ++x)
 #pragma unroll
                         for (int y = 0; y < 4; ++y) {
                             const int i = 4 * bi + x, j = 4 * bj + y;
-                            sA[i * PF + j] = accA[x][y];
+                            sA[i * PF + j] = sBeta[i] * accA[x][y];
                             if (FW) sP[i * PF + j] = accP[x][y];
                         }
-            }
-            __syncthreads();
-            if (below && half == 0)
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-#pragma unroll
-                    for (int y = 0; y < 4; ++y) {
-                        const int i = 4 * bi + x, j = 4 * bj + y;
-                        sA[i * PF + j] = sBeta[i] * (accA[x][y] + sA[i * PF + j]);
-                        if (FW) sP[i * PF + j] = accP[x][y] + sP[i * PF + j];
-                    }
-            if (w == 3) {
+            } else {
                 const int b = l >> 2, qc = l & 3;  // tile (b, b), channel quarter qc
                 float dA[4][4], dP[4][4];
 #pragma unroll
@@ -388,17 +395,15 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                             }
                     }
                 }
-                auto quad_sum = [](float v) {
-                    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-                    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-                };
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
 #pragma unroll
-                    for (int y = 0; y <= x; ++y) {
-                        dA[x][y] = quad_sum(dA[x][y]);
-                        if (FW) dP[x][y] = quad_sum(dP[x][y]);
-                    }
+                    for (int y = 0; y <= x; ++y)
+#pragma unroll
+                        for (int st = 0; st < 2; ++st) {
+                            dA[x][y] = dpp_add(dA[x][y], st);
+                            if (FW) dP[x][y] = dpp_add(dP[x][y], st);
+                        }
                 if (qc == 0)
 #pragma unroll
                     for (int x = 0; x < 4; ++x)
@@ -409,6 +414,55 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                             if (FW) sP[i * PF + j] = (y <= x) ? dP[x][y] : 0.f;
                         }
             }
+            {
+                // off-diagonal 16-blocks: row block RB against one or two column blocks
+                const int RB = w == 0 ? 1 : (w == 1 ? 2 : 3), r = 16 * RB - 1;
+                const int cb0 = w == 3 ? 0 : RB - 1, cb1 = RB - 2;
+                const bool two = (w == 1 || w == 2);
+                f32x4 oA[2] = {zero4(), zero4()}, oP[2] = {zero4(), zero4()};
+#pragma unroll 1
+                for (int kb = 0; kb < NKB; ++kb) {
+                    float kx[8], gx[8], gr[8], qx[8];
+                    load_perm_f32(sK, PKF, 16 * RB + li, 32 * kb, g, kx);
+                    load_perm_f32(sG, PKF, 16 * RB + li, 32 * kb, g, gx);
+                    load_perm_f32(sG, PKF, r, 32 * kb, g, gr);
+                    if (FW) load_perm_f32(sQ, PKF, 16 * RB + li, 32 * kb, g, qx);
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        const float e = __expf(gx[s] - gr[s]);
+                        kx[s] *= e;
+                        if (FW) qx[s] *= e;
+                    }
+                    bf16x8 kh, kl, qh, ql;
+                    split8(kx, kh, kl);
+                    if (FW) split8(qx, qh, ql);
+#pragma unroll
+                    for (int o = 0; o < 2; ++o) {
+                        if (o == 1 && !two) break;
+                        const int cb = o == 0 ? cb0 : cb1;
+                        float kj[8], gj[8];
+                        load_perm_f32(sK, PKF, 16 * cb + li, 32 * kb, g, kj);
+                        load_perm_f32(sG, PKF, 16 * cb + li, 32 * kb, g, gj);
+#pragma unroll
+                        for (int s = 0; s < 8; ++s) kj[s] *= __expf(gr[s] - gj[s]);
+                        bf16x8 jh, jl;
+                        split8(kj, jh, jl);
+                        oA[o] = mma3(oA[o], kh, kl, jh, jl, true, true);
+                        if (FW) oP[o] = mma3(oP[o], qh, ql, jh, jl, true, true);
+                    }
+                }
+#pragma unroll
+                for (int o = 0; o < 2; ++o) {
+                    if (o == 1 && !two) break;
+                    const int j = 16 * (o == 0 ? cb0 : cb1) + li;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int i = 16 * RB + 4 * g + s;
+                        sA[i * PF + j] = sBeta[i] * oA[o][s];
+                        if (FW) sP[i * PF + j] = oP[o][s];
+                    }
+                }
+            }
             if (FW)  // the strictly upper tiles of P are zero
                 for (int e = t; e < 64 * 64; e += NT) {
                     const int i = e >> 6, j = e & 63;
@@ -418,14 +472,26 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
         __syncthreads();
         // The chain step's operands, formed once per element (the scores above were the last
         // readers of K, Q and G as such): K e^{G} over K, Q e^{G} over Q, and
-        // K e^{G_last - G} over G.  The inverse below neither reads nor writes these arrays,
-        // and ends with a barrier.
-        for (int e = t; e < 64 * DK; e += NT) {
-            const int i = e / DK, c = e - i * DK;
-            const float G = sG[i * PKF + c], K = sK[i * PKF + c], eg = __expf(G);
-            sK[i * PKF + c] = K * eg;
-            if (FW) sQ[i * PKF + c] *= eg;
-            sG[i * PKF + c] = K * __expf(sGL[c] - G);
+        // (K e^{G_last - G})^T over G, transposed so that the state update reads its operand
+        // rows as 16-byte runs; the transposed writes wait until every thread has read its G.
+        // The inverse below neither reads nor writes these arrays, and ends with a barrier.
+        {
+            constexpr int PER = 64 * DK / NT;
+            float kl[PER];
+#pragma unroll
+            for (int r = 0; r < PER; ++r) {
+                const int e = t + r * NT, i = e / DK, c = e - i * DK;
+                const float G = sG[i * PKF + c], K = sK[i * PKF + c], eg = __expf(G);
+                sK[i * PKF + c] = K * eg;
+                if (FW) sQ[i * PKF + c] *= eg;
+                kl[r] = K * __expf(sGL[c] - G);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < PER; ++r) {
+                const int e = t + r * NT, i = e / DK, c = e - i * DK;
+                sG[c * PF + i] = kl[r];
+            }
         }
         {
             // the four diagonal-block inverses of I + A, one per wave, into sT (fp32)
@@ -548,12 +614,10 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
             const f32x4 eg = *(const f32x4 *)(sEG + 16 * ct + 4 * g);
 #pragma unroll
             for (int m = 0; m < NVT; ++m) S[m][ct] *= eg;
-            const int c = 16 * ct + li;
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb) {
                 float x[8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) x[s] = sG[(32 * jb + perm_k(g, s)) * PKF + c];  // K e^{G_last - G}
+                load_perm_f32(sG, PF, 16 * ct + li, 32 * jb, g, x);  // (K e^{G_last - G})^T
                 bf16x8 ah, alo;
                 split8(x, ah, alo);
 #pragma unroll

@@ -47,7 +47,8 @@ def _extreme_inputs(w):
 
 
 @pytest.mark.parametrize("dtype,dk,gate,lb", [("bf16", 128, 1, -5.0), ("bf16", 64, 1, -5.0), ("bf16", 128, 1, -5.3),
-                                              ("f32", 64, 0, -5.0), ("f32", 64, 1, -5.0)])
+                                              ("f32", 64, 0, -5.0), ("f32", 64, 1, -5.0), ("f32", 128, 0, -5.0),
+                                              ("bf16", 128, 0, -5.0)])
 def test_extreme_gates_against_oracle(dtype, dk, gate, lb):
     """bound -5.3 is the edge of the fast kernel's range: a 16-token block at the floor
     decays by e^-84.8, whose reciprocal is near the top of the fp32 and bf16 range."""
