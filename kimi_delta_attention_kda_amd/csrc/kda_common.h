@@ -23,32 +23,47 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Two fp32 values rounded to bf16 (nearest even) into one packed register, and the
+// two halves widened back exactly (a bf16 is the upper half of an fp32).  Written on the
+// packed word so that one conversion serves a pair and the widening is a shift or a mask.
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
+}
+__device__ __forceinline__ float bf_lo(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t p) { return __builtin_bit_cast(float, p & 0xffff0000u); }
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ bf16x4 bf4(f32x4 x) {
-    bf16x4 r;
-    r[0] = (bf16_t)x[0];
-    r[1] = (bf16_t)x[1];
-    r[2] = (bf16_t)x[2];
-    r[3] = (bf16_t)x[3];
-    return r;
+    return __builtin_bit_cast(bf16x4, u32x2{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])});
 }
 
 __device__ __forceinline__ f32x4 f4(bf16x4 x) {
-    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    const u32x2 p = __builtin_bit_cast(u32x2, x);
+    return f32x4{bf_lo(p[0]), bf_hi(p[0]), bf_lo(p[1]), bf_hi(p[1])};
 }
 
 // hi = RNE(x), lo = RNE(x - hi): x ~= hi + lo to about 16 significant bits.
 __device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
-    hi = bf4(x);
-    lo = bf4(x - f4(hi));
+    const uint32_t h0 = pack_bf2(x[0], x[1]), h1 = pack_bf2(x[2], x[3]);
+    hi = __builtin_bit_cast(bf16x4, u32x2{h0, h1});
+    lo = __builtin_bit_cast(bf16x4, u32x2{pack_bf2(x[0] - bf_lo(h0), x[1] - bf_hi(h0)),
+                                          pack_bf2(x[2] - bf_lo(h1), x[3] - bf_hi(h1))});
 }
 
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
+    u32x4 h, l;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        bf16_t h = (bf16_t)x[s];
-        hi[s] = h;
-        lo[s] = (bf16_t)(x[s] - (float)h);
+    for (int s = 0; s < 4; ++s) {
+        const uint32_t p = pack_bf2(x[2 * s], x[2 * s + 1]);
+        h[s] = p;
+        l[s] = pack_bf2(x[2 * s] - bf_lo(p), x[2 * s + 1] - bf_hi(p));
     }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
