@@ -234,17 +234,19 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                     const int i = RH * part + r0 + r;
                     const int64_t row = t0 + min(i, n - 1);
                     rg[r] = a.raw_gate[(row * H + h) * DK + c];
+                    // unconditional (rows past the end repeat the last row, zeroed below), so
+                    // that no load waits inside a branch for its widening
                     const int64_t kbase = (row * a.Hk + hk) * DK + c;
-                    kk[r] = i < n ? ld_in<IN16>(a.k, kbase) : 0.f;
-                    qq[r] = (FW && i < n) ? ld_in<IN16>(a.q, kbase) : 0.f;
+                    kk[r] = ld_in<IN16>(a.k, kbase);
+                    qq[r] = FW ? ld_in<IN16>(a.q, kbase) : 0.f;
                 }
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
                     const int i = RH * part + r0 + r;
                     if (i < n) G += gate_log_alpha(rg[r], dtb, Ah, safe, lb);
                     sG[i * PKF + c] = G;  // this part's own running sum for now
-                    sK[i * PKF + c] = kk[r];
-                    if (FW) sQ[i * PKF + c] = qq[r];
+                    sK[i * PKF + c] = i < n ? kk[r] : 0.f;
+                    if (FW) sQ[i * PKF + c] = i < n ? qq[r] : 0.f;
                 }
             }
             sX[part * DK + c] = G;  // this part's total
@@ -315,6 +317,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 for (int x = 0; x < 4; ++x)
 #pragma unroll
                     for (int y = 0; y < 4; ++y) { accA[x][y] = 0.f; accP[x][y] = 0.f; }
+#pragma unroll 2
                 for (int c = part * CPP; c < (part + 1) * CPP; c += CPS) {
                     fv Ki[4], Qi[4], Gi[4], Kj[4], Gj[4];
 #pragma unroll
