@@ -509,6 +509,28 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
         __syncthreads();
 
         // ---- chain step, all products split three ways
+        // dk = 128 forward: the value rows of the chunk are requested here, ahead of their use
+        // after Y, bf16 pairs sharing a register (rows past the end repeat the last row;
+        // their beta is 0)
+        typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+        [[maybe_unused]] us2 vpk[L::VG && IN16 ? NVT : 1][4][2];
+        [[maybe_unused]] float vf[L::VG && !IN16 ? NVT : 1][4][4];
+        if constexpr (L::VG) {
+#pragma unroll
+            for (int m = 0; m < NVT; ++m) {
+                const int64_t cbase = (int64_t)h * DV + col0 + 16 * (w * NVT + m) + li;
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int64_t idx = (int64_t)(t0 + min(16 * rt + 4 * g + s, n - 1)) * H * DV + cbase;
+                        if constexpr (IN16)
+                            vpk[m][rt][s >> 1][s & 1] = ((const unsigned short *)a.v)[idx];
+                        else
+                            vf[m][rt][s] = ((const float *)a.v)[idx];
+                    }
+            }
+        }
         bf16x8 Sh[NVT][NKB], Sl[NVT][NKB];
 #pragma unroll
         for (int m = 0; m < NVT; ++m)
@@ -550,12 +572,15 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 f32x4 vv;
-                if constexpr (L::VG) {
-                    // rows past the end repeat the last row; their beta is 0
+                if constexpr (L::VG && IN16) {
 #pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        vv[s] = ld_in<IN16>(a.v, ((int64_t)(t0 + min(16 * rt + 4 * g + s, n - 1)) * H + h) * DV +
-                                                     col0 + vcol);
+                    for (int s = 0; s < 4; ++s) {
+                        const uint32_t p = __builtin_bit_cast(uint32_t, vpk[m][rt][s >> 1]);
+                        vv[s] = (s & 1) ? bf_hi(p) : bf_lo(p);
+                    }
+                } else if constexpr (L::VG) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) vv[s] = vf[m][rt][s];
                 } else {
                     vv = *(const f32x4 *)(sVT + vcol * PF + 16 * rt + 4 * g);
                 }
