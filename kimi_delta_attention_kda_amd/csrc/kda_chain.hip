@@ -105,19 +105,17 @@ __device__ __forceinline__ f32x4 mma3(f32x4 acc, bf16x8 ah, bf16x8 al, bf16x8 bh
 // (I + A_bb)^-1 of one 16x16 diagonal block, by right-looking substitution on the 64
 // lanes of a wave: column c = l/4 of the inverse lives on the four lanes of a quad, lane
 // quarter q holding rows 4q .. 4q+3 as acc = -x.  Step K takes acc_K from quad lane K/4
-// (a DPP quad broadcast) and folds x_K into the rows below K; the entries of A on and
-// above the diagonal are not read (the scores leave the upper tiles of a block unwritten).
-// Ab points at the block's first entry of A (fp32, row pitch PF).
-template <int PF, int K>
-__device__ __forceinline__ void diag_inv_step(float (&acc)[4], const float *Ab, int q) {
+// (a DPP quad broadcast) and folds x_K into the rows below K.  The lane's four rows of the
+// block arrive in arow up front; the entries on and above the diagonal are zero (the
+// diagonal tiles are written with zeros there, the upper tiles are zeroed once), so a step
+// updates every row without a mask.
+template <int K>
+__device__ __forceinline__ void diag_inv_step(float (&acc)[4], const f32x4 (&arow)[4][4]) {
     const float yk = __builtin_bit_cast(
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc[K & 3]), (K >> 2) * 0x55, 0xF, 0xF, false));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float a = 4 * q + j > K ? Ab[(4 * q + j) * PF + K] : 0.f;
-        acc[j] = fmaf(-a, yk, acc[j]);
-    }
-    if constexpr (K < 15) diag_inv_step<PF, K + 1>(acc, Ab, q);
+    for (int j = 0; j < 4; ++j) acc[j] = fmaf(-arow[j][K >> 2][K & 3], yk, acc[j]);
+    if constexpr (K < 15) diag_inv_step<K + 1>(acc, arow);
 }
 
 // v_mfma_f32_16x16x16_bf16: D[16x16] += A[16x16] B[16x16]; lane (g, li): A slot s =
@@ -203,6 +201,15 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
     float *sP = (float *)(smem + L::P);
     float *sT = (float *)(smem + L::T);
     float *sVT = (float *)(smem + L::VT);
+
+    // Entries that no chunk writes, zeroed once (the first chunk's barriers publish them):
+    // the 4x4 tiles above the diagonal inside the diagonal 16-blocks of A, which the block
+    // inverses read as zeros, and the strictly upper 4x4 tiles of P.
+    for (int e = t; e < 64 * 64; e += NT) {
+        const int i = e >> 6, j = e & 63;
+        if ((j >> 4) == (i >> 4) && (j >> 2) > (i >> 2)) sA[i * PF + j] = 0.f;
+        if (FW && (j >> 2) > (i >> 2)) sP[i * PF + j] = 0.f;
+    }
 
     for (int ck = 0; ck < n_chunks; ++ck) {
         const int t0 = t_begin + ck * CH;
@@ -466,11 +473,6 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                     }
                 }
             }
-            if (FW)  // the strictly upper tiles of P are zero
-                for (int e = t; e < 64 * 64; e += NT) {
-                    const int i = e >> 6, j = e & 63;
-                    if ((j >> 2) > (i >> 2)) sP[i * PF + j] = 0.f;
-                }
         }
         __syncthreads();
         // The chain step's operands, formed once per element (the scores above were the last
@@ -502,7 +504,13 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
             float acc[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j] = (4 * q + j == c) ? -1.f : 0.f;
-            diag_inv_step<PF, 0>(acc, sA + 16 * w * PF + 16 * w, q);
+            f32x4 arow[4][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    arow[j][kb] = *(const f32x4 *)(sA + (16 * w + 4 * q + j) * PF + 16 * w + 4 * kb);
+            diag_inv_step<0>(acc, arow);
 #pragma unroll
             for (int j = 0; j < 4; ++j) sT[(16 * w + 4 * q + j) * PF + 16 * w + c] = -acc[j];
         }
