@@ -551,25 +551,38 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 Sl[m][kb] = cat(l0, l1);
             }
         f32x4 Y[NVT][4], Z[NVT][4];
+        {
+            // software-pipelined over the (row tile, k block) steps: the operand rows of step
+            // st + 1 are requested before the products of step st
+            float xk[8], xq[8], nk[8], nq[8];
+            load_perm_f32(sK, PKF, li, 0, g, xk);  // K e^{G}
+            if (FW) load_perm_f32(sQ, PKF, li, 0, g, xq);  // Q e^{G}
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+            for (int st = 0; st < 4 * NKB; ++st) {
+                const int rt = st / NKB, kb = st % NKB;
+                if (kb == 0)
 #pragma unroll
-            for (int m = 0; m < NVT; ++m) { Y[m][rt] = zero4(); Z[m][rt] = zero4(); }
-            const int row = 16 * rt + li;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                float x[8];
-                load_perm_f32(sK, PKF, row, 32 * kb, g, x);  // K e^{G}
+                    for (int m = 0; m < NVT; ++m) { Y[m][rt] = zero4(); Z[m][rt] = zero4(); }
+                if (st + 1 < 4 * NKB) {
+                    const int row = 16 * ((st + 1) / NKB) + li, k0 = 32 * ((st + 1) % NKB);
+                    load_perm_f32(sK, PKF, row, k0, g, nk);
+                    if (FW) load_perm_f32(sQ, PKF, row, k0, g, nq);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this step's work
                 bf16x8 ah, alo;
-                split8(x, ah, alo);
+                split8(xk, ah, alo);
 #pragma unroll
                 for (int m = 0; m < NVT; ++m) Y[m][rt] = mma3(Y[m][rt], ah, alo, Sh[m][kb], Sl[m][kb], true, true);
                 if (FW) {
-                    load_perm_f32(sQ, PKF, row, 32 * kb, g, x);  // Q e^{G}
-                    split8(x, ah, alo);
+                    split8(xq, ah, alo);
 #pragma unroll
                     for (int m = 0; m < NVT; ++m)
                         Z[m][rt] = mma3(Z[m][rt], ah, alo, Sh[m][kb], Sl[m][kb], true, true);
+                }
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    xk[s] = nk[s];
+                    if (FW) xq[s] = nq[s];
                 }
             }
         }
@@ -645,21 +658,36 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 }
             }
         }
+        {
+            // software-pipelined over the key tiles: the operand rows of tile ct + 1 are
+            // requested before the products of tile ct
+            f32x4 eg[NCT];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const f32x4 eg = *(const f32x4 *)(sEG + 16 * ct + 4 * g);
+            for (int ct = 0; ct < NCT; ++ct) eg[ct] = *(const f32x4 *)(sEG + 16 * ct + 4 * g);
+            float xc[2][8], xn[2][8];
 #pragma unroll
-            for (int m = 0; m < NVT; ++m) S[m][ct] *= eg;
+            for (int jb = 0; jb < 2; ++jb) load_perm_f32(sG, PF, li, 32 * jb, g, xc[jb]);  // (K e^{G_last - G})^T
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                float x[8];
-                load_perm_f32(sG, PF, 16 * ct + li, 32 * jb, g, x);  // (K e^{G_last - G})^T
-                bf16x8 ah, alo;
-                split8(x, ah, alo);
+            for (int ct = 0; ct < NCT; ++ct) {
+                if (ct + 1 < NCT)
 #pragma unroll
-                for (int m = 0; m < NVT; ++m)
-                    S[m][ct] = mma3(S[m][ct], ah, alo, cat(Uh[m][2 * jb], Uh[m][2 * jb + 1]),
-                                    cat(Ul[m][2 * jb], Ul[m][2 * jb + 1]), true, true);
+                    for (int jb = 0; jb < 2; ++jb) load_perm_f32(sG, PF, 16 * (ct + 1) + li, 32 * jb, g, xn[jb]);
+                __builtin_amdgcn_sched_barrier(0);  // keep those reads ahead of this tile's work
+#pragma unroll
+                for (int m = 0; m < NVT; ++m) S[m][ct] *= eg[ct];
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    bf16x8 ah, alo;
+                    split8(xc[jb], ah, alo);
+#pragma unroll
+                    for (int m = 0; m < NVT; ++m)
+                        S[m][ct] = mma3(S[m][ct], ah, alo, cat(Uh[m][2 * jb], Uh[m][2 * jb + 1]),
+                                        cat(Ul[m][2 * jb], Ul[m][2 * jb + 1]), true, true);
+                }
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) xc[jb][s] = xn[jb][s];
             }
         }
         __syncthreads();
