@@ -27,6 +27,8 @@
 // gate): fp32 inputs, and bf16 inputs with the original gate or a bound below -5.3.
 // Segment summaries run the same walk on the augmented state X = [M | U] with
 // X_0 = [I | 0] and value rows [0 | V] (KDA Context Parallelism, "Theory").
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -211,13 +213,59 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
         if (FW && (j >> 2) > (i >> 2)) sP[i * PF + j] = 0.f;
     }
 
+    // Cross-chunk prefetch (every instance but the register-tight dk = 128 forward pass): the
+    // inputs of chunk ck + 1 are requested before the state update of chunk ck and land in
+    // these registers while it runs.  Same rows and ownership as the load phase below.
+    constexpr bool PFX = !(FW && DK == 128);
+    constexpr int TPC = NT / DK, RH = 64 / TPC;
+    // q/k/v travel as stored (bf16 bits or fp32) and are widened when consumed, so that no
+    // conversion waits for its load at the request
+    typedef typename std::conditional<IN16, unsigned short, float>::type raw_t;
+    auto widen = [](raw_t x) -> float {
+        if constexpr (IN16)
+            return __builtin_bit_cast(float, (uint32_t)x << 16);
+        else
+            return x;
+    };
+    [[maybe_unused]] float nrg[PFX ? RH : 1];
+    [[maybe_unused]] raw_t nkk[PFX ? RH : 1], nqq[PFX && FW ? RH : 1];
+    [[maybe_unused]] raw_t nxv[PFX && !L::VG ? NVT : 1][16];
+    [[maybe_unused]] float nbl = 0.f;
+    [[maybe_unused]] auto fetch = [&](int ckf) {
+        const int tf = t_begin + ckf * CH, nf = min(CH, t_end - tf);
+        const int c = t % DK, part = t / DK;
+        if (t < 64) nbl = a.beta_logits[(int64_t)(tf + min(t, nf - 1)) * H + h];
+#pragma unroll
+        for (int r = 0; r < RH; ++r) {
+            const int64_t row = tf + min(RH * part + r, nf - 1);
+            nrg[r] = a.raw_gate[(row * H + h) * DK + c];
+            const int64_t kbase = (row * a.Hk + hk) * DK + c;
+            nkk[r] = ((const raw_t *)a.k)[kbase];
+            if constexpr (FW) nqq[r] = ((const raw_t *)a.q)[kbase];
+        }
+        if constexpr (!L::VG)
+#pragma unroll
+            for (int m = 0; m < NVT; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    nxv[m][r] = has_v ? ((const raw_t *)a.v)[((int64_t)(tf + min(16 * w + r, nf - 1)) * H + h) * DV +
+                                                              col0 + l + 64 * m]
+                                      : raw_t(0);
+    };
+    if constexpr (PFX)
+        if (n_chunks > 0) fetch(0);
+
     for (int ck = 0; ck < n_chunks; ++ck) {
         const int t0 = t_begin + ck * CH;
         const int n = min(CH, t_end - t0);
 
         // beta of the chunk rows (0 beyond the sequence end)
         if (t < 64) {
-            const float x = a.beta_logits[(int64_t)(t0 + min(t, n - 1)) * H + h];
+            float x;
+            if constexpr (PFX)
+                x = nbl;
+            else
+                x = a.beta_logits[(int64_t)(t0 + min(t, n - 1)) * H + h];
             sBeta[t] = (t < n) ? beta_of(x, a.beta_mode) : 0.f;
         }
 
@@ -229,7 +277,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
         {
             // RB rows per batch of loads: all RH at once, or two batches in the dk = 128
             // forward pass, whose registers allow no more
-            constexpr int TPC = NT / DK, RH = 64 / TPC, RB = (FW && DK == 128) ? RH / 2 : RH;
+            constexpr int RB = (FW && DK == 128) ? RH / 2 : RH;
             const int c = t % DK, part = t / DK;
             const float dtb = a.dt_bias[h * DK + c];
             float G = 0.f;
@@ -238,6 +286,12 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 float rg[RB], kk[RB], qq[RB];
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
+                    if constexpr (PFX) {  // prefetched (RB == RH)
+                        rg[r] = nrg[r];
+                        kk[r] = widen(nkk[r]);
+                        qq[r] = FW ? widen(nqq[r]) : 0.f;
+                        continue;
+                    }
                     const int i = RH * part + r0 + r;
                     const int64_t row = t0 + min(i, n - 1);
                     rg[r] = a.raw_gate[(row * H + h) * DK + c];
@@ -276,7 +330,10 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int i = 16 * w + r;
-                    xv[r] = has_v ? ld_in<IN16>(a.v, ((int64_t)(t0 + min(i, n - 1)) * H + h) * DV + col0 + vv) : 0.f;
+                    if constexpr (PFX)
+                        xv[r] = widen(nxv[m][r]);
+                    else
+                        xv[r] = has_v ? ld_in<IN16>(a.v, ((int64_t)(t0 + min(i, n - 1)) * H + h) * DV + col0 + vv) : 0.f;
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -658,6 +715,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 }
             }
         }
+        if constexpr (PFX)
+            if (ck + 1 < n_chunks) fetch(ck + 1);
         {
             // software-pipelined over the key tiles: the operand rows of tile ct + 1 are
             // requested before the products of tile ct
