@@ -6,8 +6,10 @@
 //   1. computes the gate (log alpha = -exp(a_log) softplus(raw + dt_bias), optionally
 //      clamped from below), its running sum G from the chunk start, and beta;
 //   2. builds the decayed key-key scores A (strictly lower) and query-key scores P (lower)
-//      elementwise, with exp of the non-positive differences G_i - G_j, so no factor
-//      e^{-G} is ever formed and any gate, however steep, stays finite;
+//      from exponentials of non-positive differences of G only, so no factor e^{-G} is
+//      ever formed and any gate, however steep, stays finite: MFMA products of operands
+//      decayed towards a row between the two blocks off the diagonal 16-blocks,
+//      elementwise inside them;
 //   3. inverts the four 16x16 diagonal blocks of the unit lower-triangular I + A (fp32);
 //   4. with the fp32 state slice S [dk, 16-column tiles] resident in MFMA accumulators:
 //        U  = (I + A)^-1 Diag(beta) (V - (K o e^G) S), by blocked forward substitution
@@ -40,8 +42,9 @@ constexpr int NT = 256;  // threads per workgroup (4 waves of 64)
 template <int DK, int DVS, int MODE>
 struct Lds {
     static constexpr bool FW = (MODE == MODE_FWD);
-    // dk = 128 forward: the value slice is read from global memory at its one use instead
-    // of being staged in LDS, which keeps the workgroup within 160 KB
+    // dk = 128 forward: the value slice goes from global memory to registers (requested
+    // ahead of the chain step) instead of being staged in LDS, which keeps the workgroup
+    // within 160 KB
     static constexpr bool VG = FW && DK == 128;
     static constexpr int PF = 64 + 4;    // fp32 pitch, [*][64]
     static constexpr int PKF = DK + 4;   // fp32 pitch, [64][DK]
