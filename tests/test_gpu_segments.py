@@ -117,6 +117,34 @@ def test_bf16_segment_summary_small(dk, gate):
         _assert_close(wl.as_f64(U[i, h]), U_ref, STATE_TOL, f"U seg={i} h={h}")
 
 
+@pytest.mark.parametrize("dtype,dk", [("f32", 128), ("f32", 64), ("bf16", 64)])
+def test_ragged_segments_precise_walk(dtype, dk):
+    """Segment lengths 0, 1, 64, 65, 1 and 700 through the precise walk (original gate): an empty
+    segment, single tokens, exactly one chunk, one chunk and a row, and a long ragged one, so
+    the walk's first and last chunks and its next-chunk requests meet every boundary case.
+    Against the oracle's segment maps; the empty segment's map is exactly (I, 0)."""
+    from kda_testlib import STATE_TOL
+    lens = [0, 1, 64, 65, 1, 700]
+    offs = [0]
+    for n in lens:
+        offs.append(offs[-1] + n)
+    w = wl.Workload("ragged_segments", (offs[-1],), 2, dk, dk, dtype, 0, n_slots=1, state_sigma=0.01,
+                    segments=len(lens), seed=6, raw_mean=-6.0, a_log_hi=0.0, beta_mean=-4.0)
+    print(f"[case] ragged segments {dtype} dk={dk} lengths={lens}", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+    inp["seg_offsets"] = torch.tensor(offs, dtype=torch.int32, device="cuda")
+    M, U = kda.segment_summary(inp["k"], inp["v"], inp["raw_gate"], inp["beta_logits"], inp["a_log"],
+                               inp["dt_bias"], inp["seg_offsets"], gate_mode="original")
+    torch.cuda.synchronize()
+    assert M.shape == (len(lens), 2, dk, dk) and U.shape == (len(lens), 2, dk, dk)
+    assert torch.equal(M[0], torch.eye(dk, device="cuda").expand(2, dk, dk))
+    assert torch.count_nonzero(U[0]) == 0
+    pairs = [(i, h) for i in range(1, len(lens)) for h in range(2)]
+    for (i, h), (M_ref, U_ref) in zip(pairs, _maps(w, inp, pairs)):
+        _assert_close(wl.as_f64(M[i, h]), M_ref, STATE_TOL, f"M seg={i} h={h}")
+        _assert_close(wl.as_f64(U[i, h]), U_ref, STATE_TOL, f"U seg={i} h={h}")
+
+
 def test_scan_scalar_example_exact():
     with open(os.path.join(GOLDEN, "scalar_three_segment.json")) as f:
         g = json.load(f)
