@@ -88,6 +88,22 @@ def dense_tile_flops(w) -> int:
     return w.T * w.H * (2 * 64 * (3 * w.dk + 2 * w.dv) + 6 * w.dk * w.dv)
 
 
+def decode_flops(w) -> int:
+    """One recurrent step per (sequence, head): decay, predict S^T k, rank-one write and
+    read-out S^T q, about 7 dk dv flops."""
+    return w.B * w.H * 7 * w.dk * w.dv
+
+
+def segment_flops(w) -> int:
+    """Algorithmic flops of one summary-and-scan pass.  Summaries: the chunk form on the
+    augmented state [M | U] of width dk + dv, per token-head C dk (scores, triangle) +
+    C (dk + dv) (triangular solve) + 2 dk (dk + dv) (prediction) + 2 dk (dk + dv) (state
+    update), C = 64.  Scan: 2 dk^2 dv per map and head."""
+    C, W = 64, w.dk + w.dv
+    per_th = C * w.dk + C * W + 4 * w.dk * W
+    return w.T * w.H * per_th + w.segments * w.H * 2 * w.dk * w.dk * w.dv
+
+
 def decode_bytes(w) -> int:
     """Compulsory HBM bytes of one decode call: each (sequence, head) reads and writes its
     fp32 state once and reads one token's q, k, v, gate pre-activations and beta logit,
@@ -107,6 +123,56 @@ def segment_bytes(w) -> int:
     maps = n * w.H * w.dk * (w.dk + w.dv) * 4
     scan = 2 * n * w.H * w.dk * w.dv * 4 + 2 * w.H * w.dk * w.dv * 4
     return inputs + 2 * maps + scan
+
+
+FP32_PEAK_TFLOPS = 157.3
+
+
+def roofline_bound(flops, nbytes, peak_tflops):
+    """The roofline that caps a launch: HBM when its arithmetic intensity (flop/B) lies
+    below the ridge point peak_flops / peak_bandwidth of its arithmetic type, else the
+    matrix-core peak."""
+    ridge = peak_tflops * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return "hbm" if flops / nbytes < ridge else "mfma"
+
+
+def timed_loop(step, steps):
+    """steps back-to-back calls between one pair of HIP events on the launch stream (no
+    idle gaps between calls); returns (host ms per call, device ms per call)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+
+def per_call_protocol(step, restore, reps=20, warm=3):
+    """Each call timed alone: warm untimed calls, then reps calls, each bracketed by its
+    own pair of HIP events; restore() (putting the touched pool slots back) runs before
+    every call, outside the events.  Returns the median and minimum in ms."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        restore()
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        restore()
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    med = ms[reps // 2] if reps % 2 else 0.5 * (ms[reps // 2 - 1] + ms[reps // 2])
+    return {"median_ms": round(med, 4), "min_ms": round(ms[0], 4), "reps": reps, "warmup": warm,
+            "slots_restored_outside_timing": True}
 
 
 def cpu_baseline(w, inp, target_s=12.0):
@@ -185,23 +251,16 @@ def main():
                       lower_bound=w.lower_bound, scale=w.scale, out=out)
 
     out = torch.empty((w.T, w.H, w.dv), dtype=inp["q"].dtype, device=dev)
+    used = torch.tensor(sorted(set(inp["indices"])), dtype=torch.long, device=dev)
+    saved = pool.index_select(0, used)
+    protocol = per_call_protocol(lambda: step(out), lambda: pool.index_copy_(0, used, saved))
     for _ in range(args.warmup):
         step(out)
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] warmup done ({args.warmup} steps); per-call median {protocol['median_ms']} ms, "
+          f"min {protocol['min_ms']} ms", file=sys.stderr, flush=True)
 
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(out)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_step, kern_ms = timed_loop(lambda: step(out), args.steps)
     tokens_s = w.T / (ms_step / 1e3)
 
     nbytes = algorithmic_bytes(w)
@@ -219,10 +278,15 @@ def main():
         "config": {"workload": w.name, "total_tokens": w.T, "sequences": w.B, "lengths": list(w.lengths),
                    "heads": w.H, "dk": w.dk, "dv": w.dv, "chunk": 64,
                    "gate": gate, "gate_lower_bound": w.lower_bound, "pool_slots": w.n_slots},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"bound": roofline_bound(fl, nbytes, BF16_PEAK_TFLOPS), "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "kda_chunk_fwd call: plan_kernel + kda_fast_kernel + piece_scan_kernel + fixup_kernel", "kernel_ms": round(kern_ms, 4),
-                     "algorithmic_bytes_per_launch": nbytes},
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "intensity_flop_per_byte": round(fl / nbytes, 1),
+                     "hbm_floor_ms": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+                     "times_hbm_floor": round(kern_ms / (nbytes / (HBM_PEAK_GBS * 1e9) * 1e3), 2)},
+        "per_call": protocol,
         "mfma": {"algorithmic_tflops": round(fl / (kern_ms / 1e3) / 1e12, 2),
                  "frac_of_bf16_peak": round(fl / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "dense_tile_frac_of_bf16_peak": round(fl_dense / (kern_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -281,20 +345,12 @@ def run_decode(args, w):
                    inp["dt_bias"], pool, inp["state_indices"], gate_mode=gate, lower_bound=w.lower_bound,
                    scale=w.scale, out=out)
 
+    used = torch.tensor(sorted(set(inp["indices"])), dtype=torch.long, device=dev)
+    saved = pool.index_select(0, used)
+    protocol = per_call_protocol(step, lambda: pool.index_copy_(0, used, saved))
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_step, kern_ms = timed_loop(step, args.steps)
     nbytes = decode_bytes(w)
     achieved = nbytes / (kern_ms / 1e3) / 1e9
     rec = {
@@ -305,10 +361,12 @@ def run_decode(args, w):
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "sequences": w.B, "heads": w.H, "dk": w.dk, "dv": w.dv,
                    "gate": gate, "gate_lower_bound": w.lower_bound, "pool_slots": w.n_slots},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"bound": roofline_bound(decode_flops(w), nbytes, FP32_PEAK_TFLOPS),
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
                      "kernel": "kda_decode_kernel", "kernel_ms": round(kern_ms, 4),
                      "algorithmic_bytes_per_launch": nbytes},
+        "per_call": protocol,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
@@ -360,22 +418,16 @@ def run_segments(args, w):
                             M=M, U=U)
         kda.affine_exclusive_scan(M, U, inp["S_init"], inc, outg, fin)
 
+    protocol = per_call_protocol(step, lambda: None)  # no state is mutated in place
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_step, kern_ms = timed_loop(step, args.steps)
     nbytes = segment_bytes(w)
+    fl = segment_flops(w)
     achieved = nbytes / (kern_ms / 1e3) / 1e9
+    peak_tf = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    bound = roofline_bound(fl, nbytes, peak_tf)
+    tflops = fl / (kern_ms / 1e3) / 1e12
     rec = {
         "metric": f"KDA segment summaries + exclusive scan tokens/s, {w.name}: {w.segments} segments, "
                   f"H={w.H} dk=dv={w.dk} {w.dtype}, {w.T} tokens",
@@ -385,13 +437,21 @@ def run_segments(args, w):
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "total_tokens": w.T, "segments": w.segments, "heads": w.H,
                    "dk": w.dk, "dv": w.dv, "gate": gate},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w),
+        "roofline": {"bound": bound,
+                     "achieved": round(tflops, 2) if bound == "mfma" else round(achieved, 1),
+                     "peak": peak_tf if bound == "mfma" else HBM_PEAK_GBS,
+                     "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                     "frac": round((tflops / peak_tf) if bound == "mfma" else (achieved / HBM_PEAK_GBS), 4),
+                     "traffic": measured_traffic(w),
+                     "flops_per_launch_algorithmic": fl,
+                     "intensity_flop_per_byte": round(fl / nbytes, 1),
+                     "hbm_achieved_gbs": round(achieved, 1), "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
                      "kernel": ("kda_fast_kernel" if w.dtype == "bf16" and w.gate_mode == 1 and w.lower_bound >= -5.3
                                 else "kda_chain_kernel") + " (summaries) + "
                                + ("kda_affine_scan_mfma" if w.dk in (64, 128) else "kda_affine_scan_kernel"),
                      "kernel_ms": round(kern_ms, 4),
                      "algorithmic_bytes_per_launch": nbytes},
+        "per_call": protocol,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

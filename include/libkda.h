@@ -7,7 +7,9 @@
  * return without synchronising.  The chunk kernels keep every intermediate of
  * a chunk in registers and LDS; only the load-balanced forward pass needs a
  * device workspace (kda_chunk_fwd_ws), which kda_chunk_fwd draws from a
- * stream-ordered memory pool owned by the library.
+ * stream-ordered memory pool owned by the library, one per device.  That pool
+ * keeps at most 256 MiB of freed workspace reserved between calls; larger
+ * workspaces are returned to the device at the next synchronisation.
  *
  * Per head the method keeps a state S [dk, dv] (key axis = rows) and for each
  * token t applies
@@ -115,6 +117,10 @@ typedef struct {
  *               length 0 leaves its slot untouched.
  *   state_indices [B]        int32, distinct slots
  *   out         [T, H, dv]   out_dtype, every row written; must not alias inputs
+ * If the device cannot hold the load-balancing workspace (out of memory), the
+ * call runs the same pass without load balancing (as kda_chunk_fwd_ws with no
+ * workspace: same contract and results up to rounding, slower when sequence
+ * lengths differ widely); any other runtime failure returns KDA_ERR_HIP.
  */
 kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, const void *v,
                          const float *raw_gate, const float *beta_logits, const float *a_log,

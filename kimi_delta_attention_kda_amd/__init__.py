@@ -94,6 +94,19 @@ def _need(t, name, dtype=None, device=None):
         raise ValueError(f"{name} must be on {device}")
 
 
+def _need_out(t, name, shape, dtype, device):
+    """A caller-provided output buffer: exact shape, dtype, device, contiguous (the C ABI
+    cannot see extents, so a short or strided buffer would be written out of bounds)."""
+    _need(t, name, dtype, device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _on_gpu(device):
+    if device.type != "cuda":
+        raise ValueError(f"libkda runs on a GPU; the tensors are on {device}")
+
+
 def make_desc(T, B, H, dk, dv, max_slots, qkv_dtype, out_dtype, gate_mode="safe", lower_bound=-5.0,
               beta_mode="logits", state_layout="K_FIRST", scale=None, Hk=None) -> KdaDesc:
     """Hk: key heads of q and k (None: as many as the value heads H)."""
@@ -152,9 +165,11 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
         raise ValueError("ranks and extents of the inputs disagree")
     odt = output_dtype or q.dtype
     if out is None:
+        _on_gpu(dev)
         out = torch.empty((T, H, dv), dtype=odt, device=dev)
     else:
-        _need(out, "out", odt, dev)
+        _need_out(out, "out", (T, H, dv), odt, dev)
+    _on_gpu(dev)
     d = make_desc(T, B, H, dk, dv, state_pool.shape[0], q.dtype, odt, gate_mode, lower_bound,
                   beta_mode, state_layout, scale, Hk)
     args = (C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(beta_logits), _ptr(a_log),
@@ -201,9 +216,11 @@ def decode(q, k, v, raw_gate, beta_logits, a_log, dt_bias, state_pool, state_ind
         raise ValueError("ranks and extents of the inputs disagree")
     odt = output_dtype or q.dtype
     if out is None:
+        _on_gpu(dev)
         out = torch.empty((B, H, dv), dtype=odt, device=dev)
     else:
-        _need(out, "out", odt, dev)
+        _need_out(out, "out", (B, H, dv), odt, dev)
+    _on_gpu(dev)
     d = make_desc(B, B, H, dk, dv, state_pool.shape[0], q.dtype, odt, gate_mode, lower_bound,
                   beta_mode, state_layout, scale, Hk)
     _check(lib().kda_decode(C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(beta_logits),
@@ -234,10 +251,16 @@ def segment_summary(k, v, raw_gate, beta_logits, a_log, dt_bias, seg_offsets, *,
     if v.shape[0] != T or raw_gate.shape != (T, H, dk) or beta_logits.shape != (T, H) \
             or a_log.shape != (H,) or dt_bias.shape != (H, dk):
         raise ValueError("ranks and extents of the inputs disagree")
+    n_alloc = max(n_seg, 0)
     if M is None:
-        M = torch.empty((max(n_seg, 0), H, dk, dk), dtype=torch.float32, device=dev)
+        M = torch.empty((n_alloc, H, dk, dk), dtype=torch.float32, device=dev)
+    else:
+        _need_out(M, "M", (n_alloc, H, dk, dk), torch.float32, dev)
     if U is None:
-        U = torch.empty((max(n_seg, 0), H, dk, dv), dtype=torch.float32, device=dev)
+        U = torch.empty((n_alloc, H, dk, dv), dtype=torch.float32, device=dev)
+    else:
+        _need_out(U, "U", (n_alloc, H, dk, dv), torch.float32, dev)
+    _on_gpu(dev)
     d = make_desc(T, 1, H, dk, dv, 1, k.dtype, k.dtype, gate_mode, lower_bound, beta_mode, Hk=Hk)
     _check(lib().kda_segment_summary(C.byref(d), _ptr(k), _ptr(v), _ptr(raw_gate), _ptr(beta_logits),
                                      _ptr(a_log), _ptr(dt_bias), _ptr(seg_offsets), int(n_seg),
@@ -256,6 +279,11 @@ def affine_exclusive_scan(M, U, S_init, incoming=None, outgoing=None, final_stat
         _need(t_, n_, torch.float32, dev)
     if M.shape != (n, H, dk, dk) or U.shape != (n, H, dk, dv) or S_init.shape != (H, dk, dv):
         raise ValueError("ranks and extents of the inputs disagree")
+    for t_, n_, shp in ((incoming, "incoming", U.shape), (outgoing, "outgoing", U.shape),
+                        (final_state, "final_state", S_init.shape)):
+        if t_ is not None:
+            _need_out(t_, n_, shp, torch.float32, dev)
+    _on_gpu(dev)
     incoming = torch.empty_like(U) if incoming is None else incoming
     outgoing = torch.empty_like(U) if outgoing is None else outgoing
     final_state = torch.empty_like(S_init) if final_state is None else final_state
@@ -290,5 +318,10 @@ def context_parallel(transition_matrices, local_contributions, initial_state):
 def validate_varlen(cu_seqlens, state_indices, total_tokens, max_slots):
     """Synchronous check of cu_seqlens / state_indices; raises ValueError when invalid."""
     B = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens.device)
+    _need(state_indices, "state_indices", torch.int32, cu_seqlens.device)
+    if cu_seqlens.dim() != 1 or tuple(state_indices.shape) != (B,):
+        raise ValueError("cu_seqlens must be [B+1] and state_indices [B]")
+    _on_gpu(cu_seqlens.device)
     _check(lib().kda_validate_varlen(_ptr(cu_seqlens), int(B), int(total_tokens), _ptr(state_indices),
                                      int(max_slots)))

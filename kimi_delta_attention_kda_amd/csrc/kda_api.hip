@@ -79,8 +79,10 @@ int current_device_cus(int *dev_out) {
     return cus[dev];
 }
 
-// Library-owned stream-ordered pool of device dev, created on first use; it keeps
-// freed blocks for reuse (release threshold = unlimited).  nullptr if unavailable.
+// Library-owned stream-ordered pool of device dev, created on first use.  Freed blocks
+// up to POOL_KEEP bytes stay reserved for reuse by later calls; anything above that is
+// returned to the device at the next synchronisation.  nullptr if unavailable.
+constexpr uint64_t POOL_KEEP = 256ull << 20;
 hipMemPool_t device_pool(int dev) {
     static std::mutex mu;
     static hipMemPool_t pools[MAX_DEV] = {};
@@ -94,7 +96,7 @@ hipMemPool_t device_pool(int dev) {
         props.location.id = dev;
         hipMemPool_t pool = nullptr;
         if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
-            uint64_t thr = UINT64_MAX;
+            uint64_t thr = POOL_KEEP;
             (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
             pools[dev] = pool;
         } else {
@@ -240,8 +242,8 @@ const char *kda_status_string(kda_status s) {
         case KDA_ERR_SHAPE: return "an extent is out of range or inconsistent";
         case KDA_ERR_DTYPE: return "unknown dtype code";
         case KDA_ERR_UNSUPPORTED:
-            return "arguments outside the supported contract (equal heads and dims, dk in {64,128}, "
-                   "bf16 prefill needs the safe gate with bound >= -5.3, f32 prefill needs dk 64)";
+            return "arguments outside the supported contract (out dtype equal to the q/k/v dtype, "
+                   "bf16 or f32; dk == dv in {64, 128}; either gate mode)";
         case KDA_ERR_ARG: return "bad mode value or scalar";
         case KDA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case KDA_ERR_DATA: return "cu_seqlens or state_indices violate their preconditions";
@@ -265,13 +267,19 @@ kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, con
             current_device_cus(&dev) > 0) {
             hipMemPool_t pool = device_pool(dev);
             void *ws = nullptr;
-            if (pool && hipMallocFromPoolAsync(&ws, need, pool, (hipStream_t)stream) == hipSuccess) {
+            const hipError_t ea = pool ? hipMallocFromPoolAsync(&ws, need, pool, (hipStream_t)stream)
+                                       : hipErrorOutOfMemory;
+            if (ea == hipSuccess) {
                 st = chunk_fwd_impl(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens,
                                     state_pool, state_indices, out, ws, need, stream);
-                (void)hipFreeAsync(ws, (hipStream_t)stream);
+                if (hipFreeAsync(ws, (hipStream_t)stream) != hipSuccess && st == KDA_OK) st = KDA_ERR_HIP;
                 return st;
             }
-            (void)hipGetLastError();  // no workspace: fall back to the unbalanced launch
+            // Only a workspace the device cannot hold falls back to the unbalanced launch
+            // (same results, no workspace); that error is consumed here so the launch
+            // check below does not report it.  Any other failure is returned.
+            if (ea != hipErrorOutOfMemory) return KDA_ERR_HIP;
+            if (pool) (void)hipGetLastError();
         }
     }
     return chunk_fwd_impl(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,

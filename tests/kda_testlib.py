@@ -36,33 +36,60 @@ def oracle_items(w, inp, items, nthreads=None):
                              nthreads=nthreads)
 
 
+REPORT = []             # one line per parity check, printed in pytest's terminal summary
+
+
+def report(line):
+    print(line, flush=True)
+    REPORT.append(line)
+
+
+ZERO_ABS = 1e-30        # a vanished reference: the result must be below this in magnitude
+
+
 def rel_out(o, o_ref):
+    """max|o - o_ref| / max|o_ref|.  Where the reference is exactly zero the relative
+    measure is undefined: the result passes (0) only if it is zero as well, up to
+    ZERO_ABS, and is infinitely wrong otherwise."""
     den = np.max(np.abs(o_ref))
-    return float(np.max(np.abs(o - o_ref)) / den) if den > 0 else float(np.max(np.abs(o)))
+    if den > 0:
+        return float(np.max(np.abs(o - o_ref)) / den)
+    return 0.0 if np.max(np.abs(o)) <= ZERO_ABS else float("inf")
 
 
 def rel_fro(S, S_ref):
+    """||S - S_ref||_F / ||S_ref||_F, with the same rule as rel_out for a zero reference."""
     den = np.linalg.norm(S_ref)
-    return float(np.linalg.norm(S - S_ref) / den) if den > 0 else float(np.linalg.norm(S))
+    if den > 0:
+        return float(np.linalg.norm(S - S_ref) / den)
+    return 0.0 if np.linalg.norm(S) <= ZERO_ABS else float("inf")
 
 
-def compare_items(w, inp, out, pool, items, nthreads=None, detail=False):
-    """Returns (worst output error, worst state error) over the sampled items, plus the
-    per-item errors when detail is set.  The final state is compared with the oracle's
-    state rounded to fp32, the precision of the pool: a state that has decayed below
-    fp32's range is zero there, and the kernel's must be too (rel_fro is then the
-    absolute norm)."""
-    ref = oracle_items(w, inp, items, nthreads)
+def compare_items(w, inp, out, pool, items, nthreads=None, detail=False, batch_tokens=1 << 21):
+    """Returns (worst output error, worst state error) over the given (sequence, head)
+    pairs, plus the per-item errors when detail is set.  The oracle runs over batches of
+    at most batch_tokens token-heads (bounded host memory).  The final state is compared
+    with the oracle's state rounded to fp32, the precision of the pool: a state that has
+    decayed below fp32's range is zero there, and the kernel's must then be zero too."""
     worst_o, worst_s = 0.0, 0.0
     per = []
-    for (b, h), (o_ref, S_ref) in zip(items, ref):
-        a, e = inp["cu"][b], inp["cu"][b + 1]
-        o = wl.as_f64(out[a:e, h])
-        S = wl.as_f64(pool[inp["indices"][b], h])
-        eo = rel_out(o, o_ref) if e > a else 0.0
-        es = rel_fro(S, S_ref.astype(np.float32).astype(np.float64))
-        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
-        per.append(((b, h), eo, es))
+    batch, ntok = [], 0
+    todo = list(items)
+    for i, (b, h) in enumerate(todo):
+        batch.append((b, h))
+        ntok += inp["cu"][b + 1] - inp["cu"][b]
+        if ntok < batch_tokens and i + 1 < len(todo):
+            continue
+        ref = oracle_items(w, inp, batch, nthreads)
+        for (bb, hh), (o_ref, S_ref) in zip(batch, ref):
+            a, e = inp["cu"][bb], inp["cu"][bb + 1]
+            o = wl.as_f64(out[a:e, hh])
+            S = wl.as_f64(pool[inp["indices"][bb], hh])
+            eo = rel_out(o, o_ref) if e > a else 0.0
+            es = rel_fro(S, S_ref.astype(np.float32).astype(np.float64))
+            worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+            per.append(((bb, hh), eo, es))
+        batch, ntok = [], 0
     return (worst_o, worst_s, per) if detail else (worst_o, worst_s)
 
 

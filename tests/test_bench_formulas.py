@@ -49,6 +49,23 @@ def test_segment_pass_compulsory_bytes():
     assert bench.segment_bytes(w) == inputs + 2 * maps + scan
 
 
+def test_segment_pass_flops_and_bound():
+    """The summaries run the chunk form on the augmented state [M | U] (width dk + dv = 256):
+    scores C dk, solve C (dk + dv), prediction and state update 2 dk (dk + dv) each; the
+    scan adds 2 dk^2 dv per map.  At ~100 flop/B the fp32 pass lies above the fp32 ridge
+    (157.3 TFLOP/s / 8 TB/s ~ 20 flop/B): its roofline is the matrix-core peak."""
+    w = wl.workload("segments_262k")
+    per = 64 * 128 + 64 * 256 + 2 * 128 * 256 + 2 * 128 * 256
+    assert per == 155648
+    fl = 262144 * 8 * per + 16 * 8 * 2 * 128 ** 3
+    assert bench.segment_flops(w) == fl
+    assert bench.roofline_bound(fl, bench.segment_bytes(w), bench.FP32_PEAK_TFLOPS) == "mfma"
+    # the bf16 prefill at ~89 flop/B lies below the bf16 ridge (~312 flop/B): HBM
+    v = wl.workload("varlen_32k")
+    assert bench.roofline_bound(bench.algorithmic_flops(v), bench.algorithmic_bytes(v),
+                                bench.BF16_PEAK_TFLOPS) == "hbm"
+
+
 def test_decode_compulsory_bytes():
     w = wl.workload("decode_512")
     assert (w.B, w.T, w.H, w.dk, w.dv) == (512, 512, 32, 128, 128)

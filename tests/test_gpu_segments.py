@@ -69,15 +69,19 @@ def _maps(w, inp, pairs):
 
 
 def _assert_close(x, ref, tol, what):
+    """Relative Frobenius error within tol; returns it (0 when the reference underflows to
+    zero and the result does too)."""
     from kda_testlib import rel_fro
     nref = np.linalg.norm(ref)
     if nref > 1e-30:
         e = rel_fro(x, ref)
         print(f"  {what}: rel_fro={e:.3e}", flush=True)
         assert e <= tol, what
-    else:  # the reference underflows to zero: the result must be (numerically) zero too
-        print(f"  {what}: reference ~0, max|x|={np.max(np.abs(x)):.3e}", flush=True)
-        assert np.max(np.abs(x)) <= 1e-30, what
+        return e
+    # the reference underflows to zero: the result must be (numerically) zero too
+    print(f"  {what}: reference ~0, max|x|={np.max(np.abs(x)):.3e}", flush=True)
+    assert np.max(np.abs(x)) <= 1e-30, what
+    return 0.0
 
 
 @pytest.mark.parametrize("name", ["segments_262k", "slow_gate"])
@@ -87,19 +91,25 @@ def test_segments_against_serial_replay(name):
     print(f"[case] {name} T={w.T} segments={w.segments} H={w.H}", flush=True)
     inp = wl.make_inputs(w, "cuda")
     M, U, inc, outg, fin = _summaries(w, inp)
-    heads = [0, w.H - 1]
+    heads = list(range(w.H))  # every head
     ref = _serial_replay(w, inp, heads)
+    worst = 0.0
     for h in heads:
         r_inc, r_out, r_fin = ref[h]
-        _assert_close(wl.as_f64(inc[:, h]), r_inc, STATE_TOL, f"incoming h={h}")
-        _assert_close(wl.as_f64(outg[:, h]), r_out, STATE_TOL, f"outgoing h={h}")
-        _assert_close(wl.as_f64(fin[h]), r_fin, STATE_TOL, f"final h={h}")
+        worst = max(worst, _assert_close(wl.as_f64(inc[:, h]), r_inc, STATE_TOL, f"incoming h={h}"),
+                    _assert_close(wl.as_f64(outg[:, h]), r_out, STATE_TOL, f"outgoing h={h}"),
+                    _assert_close(wl.as_f64(fin[h]), r_fin, STATE_TOL, f"final h={h}"))
         # exclusive: incoming[0] is exactly the supplied initial state
         assert torch.equal(inc[0, h], inp["S_init"][h])
-    pairs = [(0, 0), (w.segments - 1, w.H - 1)]
+    # every segment's map once, the heads taken in turn
+    pairs = [(i, i % w.H) for i in range(w.segments)]
+    wm = 0.0
     for (i, h), (M_ref, U_ref) in zip(pairs, _maps(w, inp, pairs)):
-        _assert_close(wl.as_f64(M[i, h]), M_ref, STATE_TOL, f"M seg={i} h={h}")
-        _assert_close(wl.as_f64(U[i, h]), U_ref, STATE_TOL, f"U seg={i} h={h}")
+        wm = max(wm, _assert_close(wl.as_f64(M[i, h]), M_ref, STATE_TOL, f"M seg={i} h={h}"),
+                 _assert_close(wl.as_f64(U[i, h]), U_ref, STATE_TOL, f"U seg={i} h={h}"))
+    from kda_testlib import report
+    report(f"{name}: incoming/outgoing/final stacks of all {w.H} heads x {w.segments} segments vs serial "
+           f"replay: worst rel_fro {worst:.3e}; M and U of {len(pairs)} segments: worst {wm:.3e}")
 
 
 @pytest.mark.parametrize("dk,gate", [(128, 1), (64, 1), (128, 0)])

@@ -49,6 +49,14 @@ def test_status_strings(L):
         assert isinstance(s, str) and s
     assert kda.status_string(0) == "ok"
     assert kda.status_string(99) == "unknown status"
+    # the contract the header states for KDA_ERR_UNSUPPORTED: out dtype equal to q/k/v,
+    # bf16 or f32, dk == dv in {64, 128}, either gate mode
+    unsup = kda.status_string(4)
+    for part in ("out dtype equal to the q/k/v dtype", "bf16 or f32", "dk == dv in {64, 128}",
+                 "either gate mode"):
+        assert part in unsup, (part, unsup)
+    hdr = open(os.path.join(ROOT, "include", "libkda.h")).read()
+    assert "qkv_dtype == out_dtype, bf16 or f32; dk == dv in {64, 128}; either gate mode" in hdr
 
 
 def _desc(**kw):
@@ -195,6 +203,44 @@ def test_python_binding_checks_before_the_library():
     with pytest.raises(ValueError):
         kda.segment_summary(q3, v4, torch.zeros(T, 4, dk), torch.zeros(T, 4), torch.zeros(4),
                             torch.zeros(4, dk), torch.tensor([0, T], dtype=torch.int32))
+
+
+def test_python_binding_checks_output_buffers():
+    """Caller-provided outputs must have the exact shape, dtype and contiguity the C ABI
+    writes (it cannot see extents), and every tensor must be on a GPU; each is refused with
+    ValueError before the library is called (these tensors live on the CPU)."""
+    T, H, dk, B = 8, 2, 64, 1
+    bf = dict(dtype=torch.bfloat16)
+    q = torch.zeros(T, H, dk, **bf)
+    args = (q, q, q, torch.zeros(T, H, dk), torch.zeros(T, H), torch.zeros(H), torch.zeros(H, dk),
+            torch.tensor([0, T], dtype=torch.int32), torch.zeros(1, H, dk, dk), torch.zeros(B, dtype=torch.int32))
+    for bad, what in ((torch.zeros(T - 1, H, dk, **bf), "shape"), (torch.zeros(T, H, dk + 1, **bf), "shape"),
+                      (torch.zeros(T, H, dk), "dtype"), (torch.zeros(T, dk, H, **bf).transpose(1, 2), "contiguous")):
+        with pytest.raises(ValueError, match="out"):
+            kda.chunk_fwd(*args, out=bad)
+    with pytest.raises(ValueError, match="GPU"):   # well-formed, but on the CPU
+        kda.chunk_fwd(*args, out=torch.zeros(T, H, dk, **bf))
+    dargs = (q[:B], q[:B], q[:B], torch.zeros(B, H, dk), torch.zeros(B, H), torch.zeros(H), torch.zeros(H, dk),
+             torch.zeros(1, H, dk, dk), torch.zeros(B, dtype=torch.int32))
+    with pytest.raises(ValueError, match="out"):
+        kda.decode(*dargs, out=torch.zeros(B + 1, H, dk, **bf))
+    sargs = (q, q, torch.zeros(T, H, dk), torch.zeros(T, H), torch.zeros(H), torch.zeros(H, dk),
+             torch.tensor([0, 4, T], dtype=torch.int32))
+    with pytest.raises(ValueError, match="M"):
+        kda.segment_summary(*sargs, M=torch.zeros(1, H, dk, dk))
+    with pytest.raises(ValueError, match="U"):
+        kda.segment_summary(*sargs, U=torch.zeros(2, H, dk, dk, dtype=torch.float64))
+    M, U, S0 = torch.zeros(3, H, dk, dk), torch.zeros(3, H, dk, dk), torch.zeros(H, dk, dk)
+    with pytest.raises(ValueError, match="incoming"):
+        kda.affine_exclusive_scan(M, U, S0, incoming=torch.zeros(2, H, dk, dk))
+    with pytest.raises(ValueError, match="outgoing"):
+        kda.affine_exclusive_scan(M, U, S0, outgoing=torch.zeros(3, H, dk, dk).transpose(2, 3))
+    with pytest.raises(ValueError, match="final_state"):
+        kda.affine_exclusive_scan(M, U, S0, final_state=torch.zeros(H, dk, dk - 1))
+    with pytest.raises(ValueError, match="GPU"):
+        kda.affine_exclusive_scan(M, U, S0)
+    with pytest.raises(ValueError, match="state_indices"):
+        kda.validate_varlen(torch.tensor([0, T], dtype=torch.int32), torch.zeros(2, dtype=torch.int32), T, 4)
 
 
 def test_key_heads_must_divide_value_heads(L):
