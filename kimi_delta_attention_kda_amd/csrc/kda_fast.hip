@@ -160,6 +160,7 @@ __global__ __launch_bounds__(Geo<DKT>::NT, 1) void kda_fast_kernel(ChainArgs a) 
         bool has_v;
         float *fin;    // [DK][DV] state of this unit: initial (init 0) and final
         bf16_t *obase = (bf16_t *)a.out;
+        int64_t orow = 0;  // token of obase's row 0 (W rows of a later piece start at its own)
         if (!a.plan) {
             if (pass > 0) break;
             const int jx = blockIdx.x >> 3;
@@ -209,6 +210,7 @@ __global__ __launch_bounds__(Geo<DKT>::NT, 1) void kda_fast_kernel(ChainArgs a) 
                 init = 1;
                 has_v = false;
                 obase = (bf16_t *)a.ws_W;
+                orow = t_begin - 64 * (int64_t)__builtin_amdgcn_readfirstlane(a.ws_piece[piece].w);
             } else {
                 fin = a.ws_U + ((int64_t)piece * H + h) * DK * DV;
                 init = 2;
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(Geo<DKT>::NT, 1) void kda_fast_kernel(ChainArgs a) 
                     // lane holds O[token 16rt + li][columns 16w + 4g .. +3]: one 8-byte store
                     const int i = 16 * rt + li;
                     if (i < n)
-                        *(bf16x4 *)(obase + ((int64_t)t0 * H + h) * DV + (unsigned)(i * (H * DV) + 16 * w + 4 * g)) =
+                        *(bf16x4 *)(obase + ((t0 - orow) * H + h) * DV + (unsigned)(i * (H * DV) + 16 * w + 4 * g)) =
                             bf4(osc * Z[rt]);
                 }
             }

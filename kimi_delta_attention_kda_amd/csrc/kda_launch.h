@@ -33,8 +33,14 @@ struct PlanLayout {
     int np_cap;   // capacity for pieces after the first
     int ent_cap;  // capacity for entities (sequences + pieces)
     int qcap;     // capacity of the queue (int2 entries)
+    int w_cap;    // capacity of the W rows, in chunks of later pieces
 };
-PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_slots);
+// Workspace of the balanced pass.  max_bytes == 0: room for every plan the planner can
+// choose (np_cap pieces, W rows for every chunk).  Otherwise the layout fits in
+// max_bytes by capping the pieces and the W rows (the planner then splits less), and
+// ok is false when not even an unsplit plan fits.
+PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_slots, size_t max_bytes = 0,
+                       bool *ok = nullptr);
 
 struct ChainArgs {
     const void *q;                // [T,Hk,dk] (FWD only)
@@ -66,7 +72,8 @@ struct ChainArgs {
     const int4 *ent;         // entity: (sequence, first chunk, end chunk, piece or -1)
     float *ws_M;             // [n_piece][H][dk][dk]
     float *ws_U;             // [n_piece][H][dk][dv]
-    void *ws_W;              // [T][H][dv] bf16, W rows of the later pieces
+    void *ws_W;              // [64 w_cap][H][dv] bf16, W rows of the later pieces, chunk-compact
+    const int4 *ws_piece;    // (first token, end token, chunks, first W chunk) of each later piece
 };
 
 // Precise chunk walk (kda_chain.hip): dk = dv in {64, 128}; the launch sets a.n_slices

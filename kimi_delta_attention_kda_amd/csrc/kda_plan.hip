@@ -50,6 +50,7 @@ struct PlanArgs {
     int4 *sseq;    // (sequence, first later piece, number of later pieces, pool slot)
     int *sorted;
     int np_cap, ent_cap;
+    int w_cap;     // chunks of later pieces the W rows can hold
 };
 
 __device__ __forceinline__ int chunks_of(const int32_t *cu, int b, int cs) {
@@ -201,20 +202,24 @@ __global__ __launch_bounds__(NT) void plan_kernel(PlanArgs p) {
     const int maxn = block_max<NT>(m_loc, red);
 
     // ---- first-piece length: smallest L >= average load with H (S + E(L)) <= n_cu L,
-    // E(L) = chunks moved into later pieces (they run twice)
+    // E(L) = chunks moved into later pieces (they run twice), such that the later pieces
+    // P(L) and their chunks E(L) fit the workspace (np_cap, w_cap).  All three conditions
+    // only get easier as L grows, and L = maxn splits nothing.
     const int64_t L0 = max((int64_t)L_MIN, ((int64_t)H * S + p.n_cu - 1) / p.n_cu);
     int L = 0;
     if (8 * (int64_t)maxn > 9 * L0) {
         int lo = (int)L0, hi = maxn;
         while (lo < hi) {  // uniform: every thread sees the same sums
             const int mid = lo + (hi - lo) / 2;
-            int64_t e = 0;
+            int64_t ep = 0;  // chunks moved (high 32 bits) and pieces (low 32 bits)
             for (int b = t; b < B; b += NT) {
                 const int n = chunks(b);
-                if (8 * (int64_t)n > 9 * (int64_t)mid) e += n - mid;
+                if (8 * (int64_t)n > 9 * (int64_t)mid)
+                    ep += ((int64_t)(n - mid) << 32) + (n - mid + mid - 1) / mid;
             }
-            const int64_t E = block_sum<NT>(e, red);
-            if ((int64_t)H * (S + E) <= (int64_t)p.n_cu * mid) hi = mid;
+            const int64_t EP = block_sum<NT>(ep, red);
+            const int64_t E = EP >> 32, P = EP & 0xffffffff;
+            if ((int64_t)H * (S + E) <= (int64_t)p.n_cu * mid && E <= p.w_cap && P <= p.np_cap) hi = mid;
             else lo = mid + 1;
         }
         L = lo;
@@ -489,6 +494,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
     struct Task {
         int key, t0, n, h;
         int64_t rowh;  // this lane's row (token, head); rows past the chunk's end repeat its last
+        int64_t roww;  // the same row of the chunk-compact W buffer
     };
     auto decode = [&](int64_t task) {
         int lo = 0, hi = n_piece - 1;  // last piece whose task range starts at or before task
@@ -506,14 +512,16 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         k.key = lo * H + k.h;
         k.t0 = pc.x + p.cs * c;
         k.n = min(p.cs, pc.y - k.t0);
-        k.rowh = (int64_t)(k.t0 + min(16 * w + li, k.n - 1)) * H + k.h;
+        const int r = min(16 * w + li, k.n - 1);
+        k.rowh = (int64_t)(k.t0 + r) * H + k.h;
+        k.roww = ((int64_t)(pc.w + c) * p.cs + r) * H + k.h;
         return k;
     };
     bf16x8 bw[DK / 32];
     bf16x4 ov[DV / 16];
     auto load = [&](const Task &k, bf16x8 (&b)[DK / 32], bf16x4 (&o)[DV / 16]) {
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) b[kb] = *(const bf16x8 *)(p.W + k.rowh * DK + 32 * kb + 8 * g);
+        for (int kb = 0; kb < DK / 32; ++kb) b[kb] = *(const bf16x8 *)(p.W + k.roww * DK + 32 * kb + 8 * g);
 #pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct) o[ct] = *(const bf16x4 *)(p.out + k.rowh * DV + 16 * ct + 4 * g);
     };
@@ -567,11 +575,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace plan
 
-PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_slots) {
+namespace {
+// Offsets of every part for given capacities; W last.
+PlanLayout layout_for(int B, int H, int dk, int dv, int np_cap, int64_t w_cap) {
     PlanLayout y;
-    // later pieces per head <= total chunks / L <= n_slots / H (L is at least the average
-    // load); twice that plus slack
-    y.np_cap = 2 * ((n_slots + H - 1) / H) + 2;
+    y.np_cap = np_cap;
+    y.w_cap = (int)w_cap;
     y.ent_cap = B + y.np_cap;
     y.qcap = (int)(2 * (int64_t)y.ent_cap * H);
     size_t o = 0;
@@ -595,8 +604,31 @@ PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_slots) {
     y.XT = o;  // X^T of the later pieces, bf16
     o = plan::align256(o + (size_t)y.np_cap * H * dk * dv * sizeof(bf16_t));
     y.W = o;
-    o = plan::align256(o + (size_t)T * H * dv * sizeof(bf16_t));
+    o = plan::align256(o + (size_t)w_cap * 64 * H * dv * sizeof(bf16_t));
     y.total = o;
+    return y;
+}
+}  // namespace
+
+PlanLayout plan_layout(int64_t T, int B, int H, int dk, int dv, int n_slots, size_t max_bytes, bool *ok) {
+    // later pieces per head <= total chunks / L <= n_slots / H (L is at least the average
+    // load); twice that plus slack.  Chunks of later pieces: at most every chunk.
+    const int np_full = 2 * ((n_slots + H - 1) / H) + 2;
+    const int64_t w_full = (T + 63) / 64 + B;
+    if (ok) *ok = true;
+    PlanLayout y = layout_for(B, H, dk, dv, np_full, w_full);
+    if (max_bytes == 0 || y.total <= max_bytes) return y;
+    // Fit max_bytes: the W rows first, then fewer pieces.
+    for (int np = np_full; np >= 0; np = np > 0 ? np / 2 : -1) {
+        y = layout_for(B, H, dk, dv, np, 0);
+        if (y.total <= max_bytes) {
+            const size_t per_chunk = (size_t)64 * H * dv * sizeof(bf16_t);
+            const int64_t wc = (int64_t)((max_bytes - y.total) / per_chunk);
+            return layout_for(B, H, dk, dv, np, wc < w_full ? wc : w_full);
+        }
+        if (np == 0) break;
+    }
+    if (ok) *ok = false;
     return y;
 }
 
@@ -618,6 +650,7 @@ hipError_t launch_planned_fwd(ChainArgs a, int dk, char *ws, const PlanLayout &l
     pa.sorted = (int *)(ws + lay.sorted);
     pa.np_cap = lay.np_cap;
     pa.ent_cap = lay.ent_cap;
+    pa.w_cap = lay.w_cap;
     if (lay.ent_cap <= plan::PT_ONE)
         hipLaunchKernelGGL(plan::plan_kernel<plan::PT_ONE>, dim3(1), dim3(plan::PT_ONE), 0, stream, pa);
     else
@@ -631,6 +664,7 @@ hipError_t launch_planned_fwd(ChainArgs a, int dk, char *ws, const PlanLayout &l
     a.ws_M = (float *)(ws + lay.M);
     a.ws_U = (float *)(ws + lay.U);
     a.ws_W = ws + lay.W;
+    a.ws_piece = pa.piece;
     e = launch_fast_planned(a, dk, fk.per_cu * n_cu, stream);
     if (e != hipSuccess) return e;
 
@@ -649,6 +683,7 @@ hipError_t launch_planned_fwd(ChainArgs a, int dk, char *ws, const PlanLayout &l
     pp.H = a.H;
     pp.v_first = a.v_first;
     pp.cs = fk.chunk;
+    if (lay.np_cap == 0) return hipSuccess;  // no room for pieces: nothing was split
     // grids sized from capacities (the counts are known on the device only): every scan
     // task of a full plan at once; surplus workgroups find no task and exit
     const int ncb = dk / 16;  // 16-column blocks of the state

@@ -5,7 +5,8 @@ Chunks are cs tokens; n_slots chunk-kernel workgroups run at once.  A sequence o
 chunks is split when n > 9L/8: a first piece of L chunks, then ceil((n - L) / L) near-equal
 later pieces (each run as two chains).  L is the smallest length >= max(4,
 ceil(H S / n_slots)) with H (S + E(L)) <= n_slots L, where S is the total of chunks and E(L)
-the chunks moved into later pieces; L then grows by 1/16 steps while the units longer
+the chunks moved into later pieces, and with E(L) <= w_cap and the later pieces P(L) <=
+np_cap (what the workspace holds); L then grows by 1/16 steps while the units longer
 than L/2 outnumber the slots.
 """
 
@@ -25,7 +26,7 @@ def later_pieces(n, L):
     return [base + (1 if i < rem else 0) for i in range(P)]
 
 
-def plan(lengths, H, n_slots, cs, l_min=4):
+def plan(lengths, H, n_slots, cs, l_min=4, np_cap=None, w_cap=None):
     n_cu = n_slots
     n = [chunks(x, cs) for x in lengths]
     S, maxn = sum(n), max(n) if n else 0
@@ -36,7 +37,9 @@ def plan(lengths, H, n_slots, cs, l_min=4):
         while lo < hi:
             mid = lo + (hi - lo) // 2
             E = sum(x - mid for x in n if 8 * x > 9 * mid)
-            if H * (S + E) <= n_cu * mid:
+            P = sum((x - mid + mid - 1) // mid for x in n if 8 * x > 9 * mid)
+            if H * (S + E) <= n_cu * mid and (w_cap is None or E <= w_cap) \
+                    and (np_cap is None or P <= np_cap):
                 hi = mid
             else:
                 lo = mid + 1
