@@ -58,7 +58,8 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = 4, /* valid but outside the supported contract           */
     KDA_ERR_ARG = 5,         /* bad mode value or scalar                           */
     KDA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed         */
-    KDA_ERR_DATA = 7         /* cu_seqlens / offsets / indices invalid (validation) */
+    KDA_ERR_DATA = 7,        /* cu_seqlens / offsets / indices invalid (validation) */
+    KDA_ERR_SCRATCH = 8      /* kda_chunk_fwd_noalloc: the plan exceeds its scratch  */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -126,6 +127,29 @@ kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, con
                          const float *raw_gate, const float *beta_logits, const float *a_log,
                          const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
                          const int32_t *state_indices, void *out, void *stream);
+
+/*
+ * kda_chunk_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same pass, with
+ * the load-balancing workspace taken from a fixed 256 MiB device array inside the
+ * library instead of an allocation.  The call allocates nothing, on the host or the
+ * device; inputs and outputs are the caller's, as for kda_chunk_fwd.
+ *   - Each device the library runs on holds its own copy of the array until the
+ *     process ends.  Every call on a device shares that device's copy: calls that
+ *     may overlap on one device (concurrent streams, other host threads) race and
+ *     must be serialised by the caller.  The array keeps the last call's contents;
+ *     nothing in it is read before the call has written it.
+ *   - When the plan's piece states and correction rows do not all fit, the planner
+ *     splits fewer sequences (same results up to rounding, less balancing).
+ *     KDA_ERR_SCRATCH, before any launch, when not even an unsplit plan's queue
+ *     fits (very many sequences x heads).
+ * Paths without a workspace (f32, the original gate, bound < -5.3) run as in
+ * kda_chunk_fwd.  Other arguments and errors as for kda_chunk_fwd.
+ */
+kda_status kda_chunk_fwd_noalloc(const kda_desc *desc, const void *q, const void *k, const void *v,
+                                 const float *raw_gate, const float *beta_logits, const float *a_log,
+                                 const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
+                                 const int32_t *state_indices, void *out, void *stream);
 
 /*
  * kda_chunk_fwd with a caller-owned workspace.  For bf16 with the safe gate

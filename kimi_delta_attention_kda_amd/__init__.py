@@ -52,6 +52,7 @@ def lib():
         dp = C.POINTER(KdaDesc)
         L.kda_chunk_fwd.argtypes = [dp] + [vp] * 12
         L.kda_chunk_fwd_ws.argtypes = [dp] + [vp] * 12 + [C.c_size_t, vp]
+        L.kda_chunk_fwd_noalloc.argtypes = [dp] + [vp] * 12
         L.kda_chunk_fwd_workspace_size.argtypes = [dp, C.POINTER(C.c_size_t)]
         L.kda_decode.argtypes = [dp] + [vp] * 11
         L.kda_segment_summary.argtypes = [dp] + [vp] * 7 + [i32, vp, vp, vp]
@@ -59,7 +60,7 @@ def lib():
         L.kda_validate_varlen.argtypes = [vp, i32, i64, vp, i32]
         L.kda_status_string.argtypes = [C.c_int]
         L.kda_status_string.restype = C.c_char_p
-        for f in ("kda_chunk_fwd", "kda_chunk_fwd_ws", "kda_chunk_fwd_workspace_size", "kda_decode",
+        for f in ("kda_chunk_fwd", "kda_chunk_fwd_ws", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_workspace_size", "kda_decode",
                   "kda_segment_summary", "kda_affine_exclusive_scan", "kda_validate_varlen"):
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -138,11 +139,12 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
     heads); value head h reads key head h // (H // Hk).
 
     workspace: "torch" (load-balanced pass, workspace from torch's allocator on the
-    current stream), "library" (kda_chunk_fwd: the library's own stream-ordered pool) or
-    "none" (no load balancing).
+    current stream), "library" (kda_chunk_fwd: the library's own stream-ordered pool),
+    "static" (kda_chunk_fwd_noalloc: the library's fixed device scratch, no allocation
+    at all; calls on one device must not overlap) or "none" (no load balancing).
     """
-    if workspace not in ("torch", "library", "none"):
-        raise ValueError("workspace must be 'torch', 'library' or 'none'")
+    if workspace not in ("torch", "library", "static", "none"):
+        raise ValueError("workspace must be 'torch', 'library', 'static' or 'none'")
     if q.dim() != 3 or v.dim() != 3:
         raise ValueError("ranks and extents of the inputs disagree")
     T, _, dk = q.shape
@@ -176,6 +178,9 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
             _ptr(dt_bias), _ptr(cu_seqlens), _ptr(state_pool), _ptr(state_indices), _ptr(out))
     if workspace == "library":
         _check(lib().kda_chunk_fwd(*args, _stream()))
+        return out
+    if workspace == "static":
+        _check(lib().kda_chunk_fwd_noalloc(*args, _stream()))
         return out
     ws, nbytes = None, 0
     if workspace == "torch":

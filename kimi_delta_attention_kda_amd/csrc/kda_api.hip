@@ -183,11 +183,14 @@ kda_status debug_check(const int32_t *offsets, int32_t n_off, int64_t total, boo
     return indices ? check_indices(indices, n_idx, max_slots) : KDA_OK;
 }
 
+// scratch: when set, the workspace is that device memory with the layout *scratch_lay
+// (the entry point without allocation), else the caller's workspace of workspace_bytes.
 kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, const void *v,
                           const float *raw_gate, const float *beta_logits, const float *a_log,
                           const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
                           const int32_t *state_indices, void *out, void *workspace,
-                          size_t workspace_bytes, void *stream) {
+                          size_t workspace_bytes, void *stream, char *scratch = nullptr,
+                          const kda::PlanLayout *scratch_lay = nullptr, int scratch_ncu = 0) {
     kda_status st = check_fwd(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
                               state_indices, out);
     if (st != KDA_OK) return st;
@@ -214,7 +217,10 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
     hipError_t e;
     if (use_fast(desc)) {
         a.n_slices = 1;
-        if (workspace && workspace_bytes > 0) {
+        if (scratch) {
+            e = kda::launch_planned_fwd(a, desc->dk, scratch, *scratch_lay, scratch_ncu, fwd_kernel(),
+                                        (hipStream_t)stream);
+        } else if (workspace && workspace_bytes > 0) {
             size_t need = 0;
             kda::PlanLayout lay;
             int n_cu = 0;
@@ -229,6 +235,26 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
         e = kda::launch_chain(a, desc->dk, desc->qkv_dtype == KDA_BF16, kda::MODE_FWD, (hipStream_t)stream);
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// ---- scratch of the entry point without allocation (kda_chunk_fwd_noalloc)
+// The load-balanced pass's workspace in a fixed device array, for callers that cannot
+// allocate.  Each device the library runs on holds its own copy until the process ends.
+// In host code the array's name is only a stand-in: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr size_t SCRATCH_BYTES = 256ull << 20;
+static __device__ __align__(256) char scratch[SCRATCH_BYTES];
+
+char *scratch_ptr(int dev) {
+    static std::mutex mu;
+    static char *ptrs[MAX_DEV] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        ptrs[dev] = (char *)p;
+    }
+    return ptrs[dev];
 }
 
 }  // namespace
@@ -247,6 +273,9 @@ const char *kda_status_string(kda_status s) {
         case KDA_ERR_ARG: return "bad mode value or scalar";
         case KDA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case KDA_ERR_DATA: return "cu_seqlens or state_indices violate their preconditions";
+        case KDA_ERR_SCRATCH:
+            return "the call needs more than the 256 MiB device scratch of kda_chunk_fwd_noalloc "
+                   "(too many sequences x heads for its plan)";
     }
     return "unknown status";
 }
@@ -284,6 +313,29 @@ kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, con
     }
     return chunk_fwd_impl(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
                           state_indices, out, nullptr, 0, stream);
+}
+
+kda_status kda_chunk_fwd_noalloc(const kda_desc *desc, const void *q, const void *k, const void *v,
+                                 const float *raw_gate, const float *beta_logits, const float *a_log,
+                                 const float *dt_bias, const int32_t *cu_seqlens, float *state_pool,
+                                 const int32_t *state_indices, void *out, void *stream) {
+    kda_status st = check_fwd(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
+                              state_indices, out);
+    if (st != KDA_OK) return st;
+    if (!planned_applies(desc))  // no workspace on these paths
+        return chunk_fwd_impl(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
+                              state_indices, out, nullptr, 0, stream);
+    int dev = 0;
+    const int cus = current_device_cus(&dev);
+    if (cus <= 0) return KDA_ERR_HIP;
+    bool fits = false;
+    const kda::PlanLayout lay = kda::plan_layout(desc->total_tokens, desc->batch, desc->num_heads, desc->dk,
+                                                 desc->dv, fwd_kernel().per_cu * cus, SCRATCH_BYTES, &fits);
+    if (!fits) return KDA_ERR_SCRATCH;
+    char *ws = scratch_ptr(dev);
+    if (!ws) return KDA_ERR_HIP;
+    return chunk_fwd_impl(desc, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
+                          state_indices, out, nullptr, 0, stream, ws, &lay, cus);
 }
 
 kda_status kda_chunk_fwd_ws(const kda_desc *desc, const void *q, const void *k, const void *v,

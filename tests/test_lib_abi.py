@@ -44,7 +44,7 @@ def test_every_declared_function_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in range(8):
+    for code in range(9):
         s = kda.status_string(code)
         assert isinstance(s, str) and s
     assert kda.status_string(0) == "ok"
@@ -140,6 +140,29 @@ def test_workspace_variant_error_paths(L):
         assert st in (OK, 6)
         if st == OK:
             assert n.value >= 128 * 4 * dk * 2
+
+
+def _fwd_noalloc(L, d, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, raw=FAKE, beta=FAKE, a_log=FAKE, dtb=FAKE, cu=FAKE, pool=FAKE,
+             idx=FAKE, out=FAKE)
+    p.update(ptrs)
+    return L.kda_chunk_fwd_noalloc(C.byref(d) if d is not None else None, p["q"], p["k"], p["v"], p["raw"],
+                                   p["beta"], p["a_log"], p["dtb"], p["cu"], p["pool"], p["idx"], p["out"],
+                                   None)
+
+
+def test_noalloc_variant_error_paths(L):
+    """The entry point without allocation validates exactly like kda_chunk_fwd, before it
+    looks at its scratch; its own status names the scratch limit."""
+    assert _fwd_noalloc(L, None) == ENULL
+    assert _fwd_noalloc(L, _desc(), out=None) == ENULL
+    assert _fwd_noalloc(L, _desc(T=-1)) == ESHAPE
+    assert _fwd_noalloc(L, _desc(dk=96, dv=96)) == EUNSUP
+    assert _fwd_noalloc(L, _desc(qkv_dtype=torch.float16)) == EDTYPE
+    assert _fwd_noalloc(L, _desc(lower_bound=0.5)) == EARG
+    assert _fwd_noalloc(L, _desc(B=0)) == OK
+    assert _fwd_noalloc(L, _desc(T=0)) == OK
+    assert "256 MiB" in kda.status_string(8) and "kda_chunk_fwd_noalloc" in kda.status_string(8)
 
 
 def _dec(L, d, **ptrs):
