@@ -670,6 +670,8 @@ void launch_fast_dk(const ChainArgs &a, int mode, dim3 grid, hipStream_t stream)
 hipError_t launch_fast(const ChainArgs &a, int dk, int mode, hipStream_t stream) {
     const int n_units = a.n_items * a.H;
     const dim3 grid(8 * a.n_slices * ((n_units + 7) / 8));
+    if (dk == 128 && mode == MODE_FWD)
+        return launch_pipe(a, grid, stream);
     if (dk == 128)
         launch_fast_dk<128>(a, mode, grid, stream);
     else if (dk == 64)
@@ -683,7 +685,7 @@ hipError_t launch_fast_planned(const ChainArgs &a, int dk, int n_cu, hipStream_t
     // persistent: one workgroup per CU (LDS allows no second one), drained queues end it
     const dim3 grid(8 * ((n_cu + 7) / 8));
     if (dk == 128)
-        launch_fast_dk<128>(a, MODE_FWD, grid, stream);
+        return launch_pipe(a, grid, stream);
     else if (dk == 64)
         launch_fast_dk<64>(a, MODE_FWD, grid, stream);
     else

@@ -39,12 +39,33 @@ __device__ __forceinline__ f16x8 fragA_perm_h(const f16_t *base, int pitch, int 
     return cath(*(const f16x4 *)p, *(const f16x4 *)(p + 16));
 }
 
+// x = hi + lo to about 22 significant bits: hi = fp16(x) and lo = fp16(x - hi), both
+// rounded to nearest even.  hi is formed two at a time by the packed conversion; lo by
+// the mixed-precision FMA, which reads hi from its fp16 half and computes x - hi (exact
+// in fp32) before rounding it to fp16 -- one instruction per element instead of a
+// widening, a subtraction and a narrowing.
+__device__ __forceinline__ uint32_t pk_h2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, h2));
+}
+// The -1 is passed in a register (an inline constant in this encoding is not read as an
+// fp32 -1).  The compiler does not count the wait states an MFMA needs after a VALU
+// instruction it sees only as inline asm writes one of its operands, so the second
+// instruction ends with its own wait.
+__device__ __forceinline__ uint32_t lo_h2(uint32_t hp, float a, float b) {
+    uint32_t r;
+    const float m1 = -1.f;
+    asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hp), "v"(m1), "v"(a));
+    asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\ts_nop 4"
+        : "+v"(r) : "v"(hp), "v"(m1), "v"(b));
+    return r;
+}
 __device__ __forceinline__ void split_h(f32x4 x, f16x4 &hi, f16x4 &lo) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        hi[s] = (f16_t)x[s];
-        lo[s] = (f16_t)fmaf((float)hi[s], -1.f, x[s]);  // x - hi, exact
-    }
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const uint32_t h0 = pk_h2(x[0], x[1]), h1 = pk_h2(x[2], x[3]);
+    hi = __builtin_bit_cast(f16x4, u2{h0, h1});
+    lo = __builtin_bit_cast(f16x4, u2{lo_h2(h0, x[0], x[1]), lo_h2(h1, x[2], x[3])});
 }
 
 // alpha = exp(-A softplus(x)) = (1 + e^x)^(-A), computed as 2^(-A log2(1 + 2^(x log2 e)));

@@ -86,6 +86,10 @@ hipError_t launch_chain(const ChainArgs &a, int dk, bool bf16_in, int mode, hipS
 hipError_t launch_fast(const ChainArgs &a, int dk, int mode, hipStream_t stream);
 // forward pass over the queues of a plan (a.plan set), one persistent workgroup per CU
 hipError_t launch_fast_planned(const ChainArgs &a, int dk, int n_cu, hipStream_t stream);
+// The forward pass at dk = dv = 128 (kda_pipe.hip): producer and chain wave groups one
+// chunk apart; grid as for launch_fast (one workgroup per (item, head), or persistent
+// over a plan's queue).
+hipError_t launch_pipe(const ChainArgs &a, dim3 grid, hipStream_t stream);
 // The chunk kernel of the bf16 forward pass: its chunk length and how many of its
 // workgroups share a CU (the planner sizes pieces in its chunks, for that many slots).
 // LDS admits one workgroup per CU at dk = 128 (155 KB) and at dk = 64 (92 KB).
