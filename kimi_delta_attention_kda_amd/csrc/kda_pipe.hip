@@ -513,9 +513,9 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
             };
 
             // ---- first half of the preparation of chunk ck (gate, running products):
-            // Kr, Qr, Kc and the block decays to LDS; Kc (fp32), V and beta kept for the
-            // second half
-            f32x4 kc[4];
+            // Kr, Qr, Kc (bf16, for the scores) and the block decays to LDS; Kr, Qr, Kc in
+            // fp32, V and beta kept in registers for the chain operands
+            f32x4 kc[4], kr[4], qr[4];  // fp32 Kc, Kr, Qr of the chunk being prepared
             bf16x4 hv[4];
             float hbeta = 0.f;
             auto prep0 = [&](int ck, const Lane &ln) {
@@ -548,7 +548,6 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                     pre[cc] = (rq >= 1 ? q0 : 1.f) * (rq >= 2 ? q1 : 1.f) * (rq >= 3 ? q2 : 1.f);
                     suf[cc] = (rq <= 2 ? q3 : 1.f) * (rq <= 1 ? q2 : 1.f) * (rq <= 0 ? q1 : 1.f);
                 }
-                f32x4 kr[4], qr[4];
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) {
                     // forward: Kr_i = K_i e^{G_i - G_(16I-1)}
@@ -601,10 +600,7 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                     // Kg = K e^{G}: Kr times the decays of the earlier blocks
                     const f32x4 fI = decay_before(sE, c0, pI);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = rbase + r;
-                        *(bf16x4 *)(sKG + i * PK + c0) = bf4(f4(*(const bf16x4 *)(sKR + i * PK + c0)) * fI);
-                    }
+                    for (int r = 0; r < 4; ++r) *(bf16x4 *)(sKG + (rbase + r) * PK + c0) = bf4(kr[r] * fI);
                 }
                 issue(nxt, 1, ln);
 #pragma unroll
@@ -685,7 +681,7 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                 issue(nxt, 3, ln);
             };
             // ---- the arrays the chain reads in its second interval: Qbar and Khat^T, formed
-            // here from Qr, the block decays and Kc before the next chunk's preparation
+            // here from Qr, Kc and the block decays before the next chunk's preparation
             // overwrites them, and P from registers
             auto store_second = [&](const Lane &ln) {
                 const int c0 = ch0 + 4 * ln.cq, rbase = 16 * pI + 4 * ln.rq;
@@ -694,10 +690,7 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                     // Khat_j = K_j e^{G_last - G_j} (Kc times the later blocks' decays)
                     const f32x4 fI = decay_before(sE, c0, pI), qS = decay_after(sE, c0, pI);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = rbase + r;
-                        *(bf16x4 *)(sQB + i * PK + c0) = bf4(f4(*(const bf16x4 *)(sQR + i * PK + c0)) * fI);
-                    }
+                    for (int r = 0; r < 4; ++r) *(bf16x4 *)(sQB + (rbase + r) * PK + c0) = bf4(qr[r] * fI);
 #pragma unroll
                     for (int cc = 0; cc < 4; ++cc)
                         *(f16x4 *)(sKH + tile_row(c0 + cc) * PJ + rbase) =
