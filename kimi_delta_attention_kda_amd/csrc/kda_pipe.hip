@@ -719,21 +719,25 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
             __syncthreads();
             prep1(0, lane_ids(), 1);
             __syncthreads();
-            for (int ck = 0; ck < n_chunks; ++ck) {
+            // The last chunk is peeled off, so that the loop body has no branch: with one,
+            // the load-wait bookkeeping merges the paths and makes prep1 wait for every
+            // load in flight, the next chunk's first group included.
+            for (int ck = 0; ck + 1 < n_chunks; ++ck) {
                 // first interval of chunk ck: the chain's Y, R and solve
                 {
                     const Lane ln = lane_ids();
                     store_second(ln);
-                    if (ck + 1 < n_chunks) {
-                        prep0(ck + 1, ln);
-                        issue(ck + 2, 0, ln);
-                    }
+                    prep0(ck + 1, ln);
+                    issue(ck + 2, 0, ln);
                 }
                 __syncthreads();
                 // second interval: the chain's output and state update
-                if (ck + 1 < n_chunks) prep1(ck + 1, lane_ids(), ck + 2);
+                prep1(ck + 1, lane_ids(), ck + 2);
                 __syncthreads();
             }
+            store_second(lane_ids());
+            __syncthreads();
+            __syncthreads();
         }
     }  // units
 }
