@@ -84,6 +84,12 @@ typedef enum { KDA_STATE_K_FIRST = 0, KDA_STATE_V_FIRST = 1 } kda_state_layout;
  * the fast chunk kernel (the gfx950 contract of kda_chunk: bf16, safe gate; its
  * 16-token factorisation of the decay needs 16*|bound| < 85); other calls run a
  * slower chunk walk that evaluates every decay factor directly, at fp32 accuracy.
+ * Magnitudes on the fast kernel: values and states may be of any finite size (the
+ * solve rescales its right-hand side by a power of two into the range of its fp16
+ * operands and undoes it exactly); the decayed score blocks beta k_i^T k_j and
+ * q_i^T k_j, and the inverses of the 16x16 diagonal blocks of I + A, are held in
+ * fp16, which assumes keys and queries of at most unit L2 norm per head (the
+ * normalisation KDA applies to q and k).  Larger keys belong on the f32 path.
  */
 typedef struct {
     int64_t total_tokens;    /* T: rows of q, k, v, raw_gate, beta_logits, out   */

@@ -139,7 +139,7 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
     heads); value head h reads key head h // (H // Hk).
 
     workspace: "torch" (load-balanced pass, workspace from torch's allocator on the
-    current stream), "library" (kda_chunk_fwd: the library's own stream-ordered pool),
+    current stream; the unbalanced launch if that allocation fails), "library" (kda_chunk_fwd: the library's own stream-ordered pool),
     "static" (kda_chunk_fwd_noalloc: the library's fixed device scratch, no allocation
     at all; calls on one device must not overlap) or "none" (no load balancing).
     """
@@ -187,8 +187,13 @@ def chunk_fwd(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_
         need = C.c_size_t(0)
         _check(lib().kda_chunk_fwd_workspace_size(C.byref(d), C.byref(need)))
         if need.value > 0:
-            ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
-            nbytes = need.value
+            try:
+                ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+                nbytes = need.value
+            except torch.OutOfMemoryError:
+                # as kda_chunk_fwd does when its pool cannot serve the workspace: the
+                # unbalanced launch, which needs none
+                ws, nbytes = None, 0
     _check(lib().kda_chunk_fwd_ws(*args, _ptr(ws), nbytes, _stream()))
     return out
 

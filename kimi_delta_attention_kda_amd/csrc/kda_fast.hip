@@ -551,13 +551,14 @@ __global__ __launch_bounds__(Geo<DKT>::NT, 1) void kda_fast_kernel(ChainArgs a) 
                 rmax = fmaxf(rmax, fmaxf(fmaxf(fabsf(Y[bI][0]), fabsf(Y[bI][1])), fmaxf(fabsf(Y[bI][2]), fabsf(Y[bI][3]))));
             }
             // U is carried as fp16 hi + lo, exact to ~2^-22 of its largest entry only while
-            // that entry is near 1: a wave whose R is small (tiny beta and a vanished state)
-            // scales R, hence U, by a power of two, undone exactly in the output scale and
-            // the state update below.
+            // that entry is near 1, and finite only below 65504: a wave whose R is small
+            // (tiny beta and a vanished state) or large (large values or states) scales R,
+            // hence U, by a power of two, undone exactly in the output scale and the state
+            // update below.
             rmax = wave_max_nonneg(rmax);
-            if (rmax < 0x1p-8f && rmax > 0.f) {
+            if ((rmax < 0x1p-8f && rmax > 0.f) || (rmax >= 0x1p6f && rmax < 0x1p127f)) {
                 // 2^k with rmax 2^k in [1/4, 1/2)
-                const int k = min(64, -2 - ((int)(__builtin_bit_cast(unsigned, rmax) >> 23) - 127));
+                const int k = max(-126, min(64, -2 - ((int)(__builtin_bit_cast(unsigned, rmax) >> 23) - 127)));
                 usc = __builtin_bit_cast(float, (k + 127) << 23);
                 iusc = __builtin_bit_cast(float, (127 - k) << 23);
 #pragma unroll

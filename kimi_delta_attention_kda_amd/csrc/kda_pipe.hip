@@ -340,13 +340,14 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                     }
                 }
                 // U travels as fp16 hi + lo, exact to ~2^-22 of its largest entry only while
-                // that entry is near 1: a wave whose R is small (tiny beta and a vanished
-                // state) scales R, hence U, by a power of two, undone exactly in the output
-                // scale and around the state update.
+                // that entry is near 1, and finite only below 65504: a wave whose R is small
+                // (tiny beta and a vanished state) or large (large values or states) scales R,
+                // hence U, by a power of two that brings max |R| into [1/4, 1/2), undone
+                // exactly in the output scale and around the state update.
                 float usc, iusc;
                 rmax = wave_max_nonneg(rmax);
-                if (rmax < 0x1p-8f && rmax > 0.f) {
-                    const int k = min(64, -2 - ((int)(__builtin_bit_cast(unsigned, rmax) >> 23) - 127));
+                if ((rmax < 0x1p-8f && rmax > 0.f) || (rmax >= 0x1p6f && rmax < 0x1p127f)) {
+                    const int k = max(-126, min(64, -2 - ((int)(__builtin_bit_cast(unsigned, rmax) >> 23) - 127)));
                     usc = __builtin_bit_cast(float, (k + 127) << 23);
                     iusc = __builtin_bit_cast(float, (127 - k) << 23);
 #pragma unroll

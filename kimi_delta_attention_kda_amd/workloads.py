@@ -88,6 +88,9 @@ def workload(name: str, seed: int = 0) -> Workload:
     if name == "varlen_32k":
         return Workload(name, _varlen_32k_lengths(rng), 32, 128, 128, "bf16", 1,
                         n_slots=64, state_sigma=0.01, seed=seed)
+    if name == "varlen_32k_original":  # the 32K lengths with the original (unclamped) gate
+        return Workload(name, _varlen_32k_lengths(rng), 32, 128, 128, "bf16", 0,
+                        n_slots=64, state_sigma=0.01, seed=seed)
     if name == "varlen_32k_dk64":
         return Workload(name, _varlen_32k_lengths(rng), 32, 64, 64, "bf16", 1,
                         n_slots=64, state_sigma=0.01, seed=seed)
@@ -106,7 +109,7 @@ def workload(name: str, seed: int = 0) -> Workload:
     raise KeyError(name)
 
 
-NAMES = ("tiny_fp32", "varlen_32k", "varlen_32k_dk64", "long_131k", "segments_262k", "short_varlen_512", "decode_512")
+NAMES = ("tiny_fp32", "varlen_32k", "varlen_32k_original", "varlen_32k_dk64", "long_131k", "segments_262k", "short_varlen_512", "decode_512")
 
 
 def custom(lengths, H=2, dk=64, dv=64, dtype="bf16", gate_mode=1, n_slots=None,

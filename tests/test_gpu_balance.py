@@ -146,6 +146,27 @@ def test_workspace_too_small_is_refused(dk):
     assert torch.equal(pool.view(torch.int32), inp["state_pool"].view(torch.int32))
 
 
+def test_torch_workspace_oom_falls_back(monkeypatch):
+    """workspace="torch" whose allocation fails runs the unbalanced launch, bit for bit."""
+    from kda_testlib import run_fwd
+    w = wl.custom((3000, 700), H=2, dk=128, dv=128, name="oom_ws", seed=21)
+    print("[case] torch workspace allocation fails", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+    real_empty = torch.empty
+
+    def empty(*a, **kw):
+        if kw.get("dtype") is torch.uint8:
+            raise torch.OutOfMemoryError("simulated workspace allocation failure")
+        return real_empty(*a, **kw)
+
+    monkeypatch.setattr(torch, "empty", empty)
+    out, pool = run_fwd(w, inp, workspace="torch")
+    monkeypatch.undo()
+    out_n, pool_n = run_fwd(w, inp, workspace="none")
+    assert torch.equal(out.view(torch.int16), out_n.view(torch.int16))
+    assert torch.equal(pool.view(torch.int32), pool_n.view(torch.int32))
+
+
 @pytest.mark.parametrize("dk", [128, 64])
 def test_random_mixes_plan_and_agreement(dk):
     """Seeded random batches (1 to 40 sequences of 1 to 20,000 tokens, 1 to 3 heads, some empty):

@@ -8,6 +8,7 @@
 - No decay at all over 4,000 tokens (the steady level of the state's rounding error).
 - Many short sequences around a few long ones: more sequences than the planner keeps in
   LDS (its global-memory paths), with pieces, against the oracle on samples.
+- Values and states far above the fp16 range of the bf16 paths' U operand.
 - No tokens: a batch of empty sequences leaves the pool untouched.
 """
 import numpy as np
@@ -113,6 +114,27 @@ def test_many_sequences_with_pieces(dk):
         s = inp["indices"][b]
         assert rel_out(wl.as_f64(out[a:e]), wl.as_f64(out_n[a:e])) <= OUT_TOL_BF16
         assert rel_fro(wl.as_f64(pool[s]), wl.as_f64(pool_n[s])) <= STATE_TOL
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_large_values_and_states(dk):
+    """bf16 v ~ N(0, 1e5^2) and initial states ~ N(0, 1e4^2): R = beta (V - Kg S) lies far
+    above the fp16 range in which the bf16 paths carry U (hi + lo parts), so the solve
+    scales R down by a power of two and undoes it exactly.  Balanced and unbalanced."""
+    from kda_testlib import compare_items, run_fwd, untouched_slots_identical, OUT_TOL_BF16, STATE_TOL
+    w = wl.custom([3000, 500, 1200], H=2, dk=dk, dv=dk, dtype="bf16", gate_mode=1, seed=15,
+                  state_sigma=1e4)
+    inp = wl.make_inputs(w, "cuda")
+    inp["v"].mul_(1e5)
+    for ws in ("torch", "none"):
+        print(f"[case] large values and states, dk={dk}, workspace={ws}", flush=True)
+        out, pool = run_fwd(w, inp, workspace=ws)
+        used = inp["state_indices"].long()
+        assert torch.isfinite(out.float()).all() and torch.isfinite(pool[used]).all()
+        eo, es = compare_items(w, inp, out, pool, [(b, h) for b in range(w.B) for h in range(w.H)])
+        print(f"  all pairs: out_err={eo:.3e} state_err={es:.3e}", flush=True)
+        assert eo <= OUT_TOL_BF16 and es <= STATE_TOL
+        assert untouched_slots_identical(inp, pool)
 
 
 @pytest.mark.parametrize("workspace", ["torch", "none"])
