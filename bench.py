@@ -29,6 +29,7 @@ METRIC = "KDA prefill tokens/s at H=32 dk=dv=128 bf16, 32K tokens; % MFMA peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILES = {"varlen_32k": os.path.join(ROOT, "profiles", "kda_chunk_fwd_varlen_32k_traffic.json"),
+                 "long_131k": os.path.join(ROOT, "profiles", "kda_chunk_fwd_long_131k_traffic.json"),
                  "decode_512": os.path.join(ROOT, "profiles", "kda_decode_kernel_decode_512_traffic.json"),
                  "segments_262k": os.path.join(ROOT, "profiles", "kda_segment_pass_segments_262k_traffic.json")}
 
@@ -46,10 +47,17 @@ def measured_traffic(w):
     return None
 
 
-def measured_utilization(w):
+def chunk_kernel(w) -> str:
+    """The chunk kernel that kda_chunk_fwd runs for workload w."""
+    if w.dtype == "bf16" and w.gate_mode == 1 and w.lower_bound >= -5.3:
+        return "kda_pipe_kernel" if w.dk == 128 else "kda_fast_kernel"
+    return "kda_chain_kernel"
+
+
+def measured_utilization(w, kernel=None):
     """MFMA- and VALU-busy fractions of the chunk kernel from the counter summary of this
     workload, while the kernel sources still hash to the measured version; else None."""
-    f = os.path.join(ROOT, "profiles", f"kda_fast_kernel_{w.name}_utilization.json")
+    f = os.path.join(ROOT, "profiles", f"{kernel or chunk_kernel(w)}_{w.name}_utilization.json")
     if not os.path.exists(f):
         return None
     with open(f) as fh:
@@ -62,9 +70,10 @@ def measured_utilization(w):
 def kernel_source_sha() -> str:
     d = os.path.join(ROOT, "kimi_delta_attention_kda_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    for f in sorted(os.listdir(d)):  # the kernel sources (subfolders hold no KDA kernel)
+        if os.path.isfile(os.path.join(d, f)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -209,6 +218,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter scale)")
+    ap.add_argument("--mfma-calibration", action="store_true",
+                    help="also run a kernel of known MFMA count (MFMA-busy counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -241,6 +252,8 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(dev)
+    if args.mfma_calibration:
+        mfma_calibration(dev)
 
     pool = inp["state_pool"]
     gate = "safe" if w.gate_mode == 1 else "original"
@@ -281,7 +294,8 @@ def main():
         "roofline": {"bound": roofline_bound(fl, nbytes, BF16_PEAK_TFLOPS), "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "kda_chunk_fwd call: plan_kernel + kda_fast_kernel + piece_scan_kernel + fixup_kernel", "kernel_ms": round(kern_ms, 4),
+                     "kernel": f"kda_chunk_fwd call: plan_kernel + {chunk_kernel(w)} + piece_scan_kernel + fixup_kernel",
+                     "kernel_ms": round(kern_ms, 4),
                      "algorithmic_bytes_per_launch": nbytes,
                      "intensity_flop_per_byte": round(fl / nbytes, 1),
                      "hbm_floor_ms": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
@@ -307,6 +321,31 @@ def copy_calibration(dev):
         dst.copy_(src)
     torch.cuda.synchronize()
     print("[bench] copy calibration: 3 x 1 GiB read + 1 GiB write", file=sys.stderr, flush=True)
+
+
+# the MFMA calibration launch: 2048 workgroups of 4 waves (8 waves per SIMD), 8192
+# instructions each
+CALIB_WG, CALIB_ITERS = 2048, 8192
+
+
+def mfma_calibration(dev):
+    """A kernel of known MFMA count, three times: the counter runs scale the MFMA-busy
+    counter by what it reads for it; its event time gives the sustained MFMA rate."""
+    import torch
+    import kimi_delta_attention_kda_amd as kda
+    out = torch.empty(CALIB_WG * 256, dtype=torch.float32, device=dev)
+    kda.calib_mfma(CALIB_WG, 16, out)  # warm-up
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(3):
+        kda.calib_mfma(CALIB_WG, CALIB_ITERS, out)
+    ev[1].record()
+    torch.cuda.synchronize()
+    n = CALIB_WG * 4 * CALIB_ITERS
+    ms = ev[0].elapsed_time(ev[1]) / 3
+    tflops = n * 2 * 16 * 16 * 32 / (ms * 1e-3) / 1e12
+    print(f"[bench] mfma calibration: {n} v_mfma_f32_16x16x32_bf16 per launch, 3 launches, "
+          f"{ms:.3f} ms per launch, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
 
 def run_decode(args, w):
@@ -336,6 +375,8 @@ def run_decode(args, w):
                "sample": f"the whole call: {w.B} sequences x {w.H} heads, one token each ({dt:.2f} s)"}
     if args.copy_calibration:
         copy_calibration(dev)
+    if args.mfma_calibration:
+        mfma_calibration(dev)
     gate = "safe" if w.gate_mode == 1 else "original"
     pool = inp["state_pool"]
     out = torch.empty((w.B, w.H, w.dv), dtype=inp["q"].dtype, device=dev)
@@ -406,6 +447,8 @@ def run_segments(args, w):
                          f"{dt:.1f} s), scaled to all heads; the scan is not included"}
     if args.copy_calibration:
         copy_calibration(dev)
+    if args.mfma_calibration:
+        mfma_calibration(dev)
     n = w.segments
     M = torch.empty((n, w.H, w.dk, w.dk), dtype=torch.float32, device=dev)
     U = torch.empty((n, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
@@ -450,7 +493,9 @@ def run_segments(args, w):
                                 else "kda_chain_kernel") + " (summaries) + "
                                + ("kda_affine_scan_mfma" if w.dk in (64, 128) else "kda_affine_scan_kernel"),
                      "kernel_ms": round(kern_ms, 4),
-                     "algorithmic_bytes_per_launch": nbytes},
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "profiled_busy": measured_utilization(w, chunk_kernel(w) if chunk_kernel(w) == "kda_chain_kernel"
+                                                           else "kda_fast_kernel")},
         "per_call": protocol,
         "cpu_baseline": cpu,
     }

@@ -67,6 +67,35 @@ def lib():
     return _lib
 
 
+CALIB_LIB_PATH = os.path.join(_HERE, "libkda_calib.so")
+_calib = None
+
+
+def calib_lib():
+    """Loads libkda_calib.so (include/kda_calib.h): a kernel of known MFMA count that scales
+    the profiler's MFMA-busy counter.  Measurement only, no part of the KDA computation."""
+    global _calib
+    if _calib is None:
+        if not os.path.exists(CALIB_LIB_PATH):
+            raise RuntimeError(f"libkda_calib.so not built ({CALIB_LIB_PATH}); run kimi_delta_attention_kda_amd/build.py")
+        L = C.CDLL(CALIB_LIB_PATH)
+        L.kda_calib_mfma.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+        L.kda_calib_mfma.restype = C.c_int
+        _calib = L
+    return _calib
+
+
+def calib_mfma(n_workgroups: int, iters: int, out: torch.Tensor) -> None:
+    """Launches the calibration kernel on the current stream: n_workgroups * 4 * iters
+    v_mfma_f32_16x16x32_bf16 instructions; out: fp32, n_workgroups * 256 elements."""
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous() \
+            or out.numel() < n_workgroups * 256:
+        raise ValueError("out must be a contiguous fp32 device tensor of n_workgroups * 256 elements")
+    code = calib_lib().kda_calib_mfma(n_workgroups, iters, _ptr(out), _stream())
+    if code != 0:
+        raise RuntimeError(f"kda_calib_mfma failed ({code})")
+
+
 def status_string(code: int) -> str:
     return lib().kda_status_string(code).decode()
 

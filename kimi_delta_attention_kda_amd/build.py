@@ -1,4 +1,5 @@
-"""Builds libkda.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc."""
+"""Builds libkda.so (HIP kernels for gfx950 + the C ABI) and libkda_calib.so (a counter
+calibration kernel) in-tree with hipcc."""
 from __future__ import annotations
 
 import os
@@ -19,18 +20,28 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+# a kernel of known MFMA count that scales the profiler's MFMA-busy counter (not KDA)
+CALIB_LIB = os.path.join(HERE, "libkda_calib.so")
+CALIB_SOURCES = ["calib/kda_calib.hip"]
+
+
+def _hipcc(out: str, sources, verbose: bool) -> None:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
+    srcs = [os.path.join(HERE, "csrc", s) for s in sources]
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libkda")
-    os.replace(tmp, LIB)
+        raise RuntimeError("hipcc failed building " + os.path.basename(out))
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(LIB, SOURCES, verbose)
+    _hipcc(CALIB_LIB, CALIB_SOURCES, verbose)
     return LIB
 
 

@@ -26,8 +26,8 @@ def L():
     return kda.lib()
 
 
-def _declared_functions():
-    src = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kda_\w+)\s*\(", src, flags=re.M)))
 
@@ -41,6 +41,19 @@ def test_every_declared_function_is_exported(L):
     for n in names:
         assert n in exported, n
         assert hasattr(L, n)
+
+
+def test_calibration_library_exports_its_header(L):
+    """libkda_calib.so (the MFMA counter calibration kernel) exports what kda_calib.h
+    declares and refuses bad arguments before any launch."""
+    names = _declared_functions(os.path.join(ROOT, "include", "kda_calib.h"))
+    assert names == ["kda_calib_mfma"]
+    nm = subprocess.run(["nm", "-D", "--defined-only", kda.CALIB_LIB_PATH], capture_output=True, text=True).stdout
+    assert set(names) <= set(re.findall(r" T (kda_\w+)$", nm, flags=re.M))
+    C_ = kda.calib_lib()
+    assert C_.kda_calib_mfma(0, 1, FAKE, None) == 1
+    assert C_.kda_calib_mfma(1, 0, FAKE, None) == 1
+    assert C_.kda_calib_mfma(1, 1, None, None) == 1
 
 
 def test_status_strings(L):
