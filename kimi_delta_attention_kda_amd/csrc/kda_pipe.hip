@@ -139,6 +139,10 @@ struct Lane {
     int l, g, li;  // MFMA layout: lane l = 16 g + li
     int rq, cq;    // producer: row quarter, 4-channel group (4 cq .. 4 cq + 3 of the wave's half)
 };
+__device__ __forceinline__ float sgpr_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 __device__ __forceinline__ Lane lane_ids() {
     int l = threadIdx.x & 63;
     asm volatile("" : "+v"(l));
@@ -175,7 +179,9 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
     const int pI = pw >> 1;        //   rows 16 pI .. 16 pI + 15 (block pI),
     const int ch0 = 64 * (pw & 1); //   key channels ch0 .. ch0 + 63
     float *sDTB = (float *)(smem + L::DTB) + (pw & 7) * (DK / 2);  // this producer wave's copy
-    const float amin = a.gate_mode == 1 ? expf(a.lb) : 0.f;  // alpha floor of the safe gate
+    // alpha floor of the safe gate; wave-uniform values computed by vector instructions
+    // are moved to scalar registers, which the producer's vector registers cannot spare
+    const float amin = sgpr_f(a.gate_mode == 1 ? expf(a.lb) : 0.f);
     const int xcd = blockIdx.x & 7;
 
     // strictly-upper blocks of P are never written below
@@ -478,7 +484,7 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
         } else {
             // ================================ the producer ================================
             // lane: rows 16 pI + 4 rq + [0, 4), key channels c0 .. c0 + 3 (c0 = ch0 + 4 cq)
-            const float negA = -expf(a.a_log[h]);
+            const float negA = sgpr_f(-expf(a.a_log[h]));
             {
                 // each producer wave keeps its own copy of its channels' dt_bias (scaled by
                 // log2 e) in LDS: read back by the same wave only, no barrier needed, and no
@@ -497,6 +503,16 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
             // Every load is unconditional (ck is clamped to the unit's last chunk, V is
             // read even where a unit does not use it): a load under a condition leaves the
             // register merged with its old value, a copy that waits for the load to land.
+            auto issue_raw = [&](int ck, const Lane &ln) {
+                ck = min(ck, n_chunks - 1);
+                const int rbase = 16 * pI + 4 * ln.rq, c0 = ch0 + 4 * ln.cq;
+                const int tq = t_begin + ck * 64;
+                const int nq = min(64, t_end - tq);
+                const int64_t rb = (int64_t)tq * H + h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    praw[r] = *(const f32x4 *)(a.raw_gate + rb * DK + (unsigned)(min(rbase + r, nq - 1) * (H * DK) + c0));
+            };
             auto issue = [&](int ck, int r, const Lane &ln) {
                 ck = min(ck, n_chunks - 1);
                 const int rbase = 16 * pI + 4 * ln.rq, c0 = ch0 + 4 * ln.cq;
@@ -506,11 +522,30 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                 const int64_t rbk = GQA ? (int64_t)tq * a.Hk + hk : rb;
                 const unsigned ro = (unsigned)(min(rbase + r, nq - 1) * (H * DK) + c0);
                 const unsigned rok = GQA ? (unsigned)(min(rbase + r, nq - 1) * (a.Hk * DK) + c0) : ro;
-                praw[r] = *(const f32x4 *)(a.raw_gate + rb * DK + ro);
                 pk[r] = *(const bf16x4 *)((const bf16_t *)a.k + rbk * DK + rok);
                 pq[r] = *(const bf16x4 *)((const bf16_t *)a.q + rbk * DK + rok);
                 pv[r] = *(const bf16x4 *)((const bf16_t *)a.v + rb * DV + ro);
                 if (r == 3) pbl = a.beta_logits[rb + (unsigned)(min(ln.l, nq - 1) * H)];
+            };
+
+            // the gate of chunk ck, in place over its raw pre-activations (praw then holds alpha);
+            // rows past the sequence end hold a copy of its last row: only their gate (alpha =
+            // 1) and beta (0) are masked; with beta = 0 they add nothing to A, R, U or the
+            // state, and their outputs are never stored
+            auto gate_of = [&](int ck, const Lane &ln) {
+                ck = min(ck, n_chunks - 1);
+                const int nq = min(64, t_end - (t_begin + ck * 64)), rbase = 16 * pI + 4 * ln.rq;
+                const f32x4 dtb = *(const f32x4 *)(sDTB + 4 * ln.cq);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float floor_r = rbase + r < nq ? amin : 1.f;
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) praw[r][cc] = gate_alpha(praw[r][cc], dtb[cc], negA, floor_r);
+                }
+                // pinned here: the compiler would otherwise sink this work past the barrier
+                // that follows, next to its use
+#pragma unroll
+                for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(praw[r]));
             };
 
             // ---- first half of the preparation of chunk ck (gate, running products):
@@ -522,17 +557,12 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
             auto prep0 = [&](int ck, const Lane &ln) {
                 const int rq = ln.rq, c0 = ch0 + 4 * ln.cq, rbase = 16 * pI + 4 * rq;
                 const int nq = min(64, t_end - (t_begin + ck * 64));
-                const f32x4 dtb = *(const f32x4 *)(sDTB + 4 * ln.cq);
-                // rows past the sequence end hold a copy of its last row: only their gate
-                // (alpha = 1) and beta (0) are masked; with beta = 0 they add nothing to A,
-                // R, U or the state, and their outputs are never stored
                 float al[4][4], kf[4][4], qf[4][4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float floor_r = rbase + r < nq ? amin : 1.f;
 #pragma unroll
                     for (int cc = 0; cc < 4; ++cc) {
-                        al[r][cc] = gate_alpha(praw[r][cc], dtb[cc], negA, floor_r);
+                        al[r][cc] = praw[r][cc];  // alpha, from gate_of
                         kf[r][cc] = (float)pk[r][cc];
                         qf[r][cc] = (float)pq[r][cc];
                     }
@@ -680,6 +710,9 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                     for (int j = 0; j < 4; ++j) sD[(pw * 16 + 4 * q + j) * PD + c] = (f16_t)(0.f - acc[j]);
                 }
                 issue(nxt, 3, ln);
+                // the gate of chunk nxt, a chunk ahead of its running products: its raw
+                // pre-activations went out before this interval
+                gate_of(nxt, ln);
             };
             // ---- the arrays the chain reads in its second interval: Qbar and Khat^T, formed
             // here from Qr, Kc and the block decays before the next chunk's preparation
@@ -712,9 +745,12 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
 
             {
                 const Lane ln = lane_ids();
+                issue_raw(0, ln);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) issue(0, r, ln);
+                gate_of(0, ln);
                 prep0(0, ln);
+                issue_raw(1, ln);
                 issue(1, 0, ln);
             }
             __syncthreads();
@@ -729,6 +765,7 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                     const Lane ln = lane_ids();
                     store_second(ln);
                     prep0(ck + 1, ln);
+                    issue_raw(ck + 2, ln);
                     issue(ck + 2, 0, ln);
                 }
                 __syncthreads();
