@@ -149,8 +149,8 @@ kda_status kda_chunk_fwd(const kda_desc *desc, const void *q, const void *k, con
  *     splits fewer sequences (same results up to rounding, less balancing).
  *     KDA_ERR_SCRATCH, before any launch, when not even an unsplit plan's queue
  *     fits (very many sequences x heads).
- * Paths without a workspace (f32, the original gate, bound < -5.3) run as in
- * kda_chunk_fwd.  Other arguments and errors as for kda_chunk_fwd.
+ * f32 inputs, which use no workspace, run as in kda_chunk_fwd.  Other arguments
+ * and errors as for kda_chunk_fwd.
  */
 kda_status kda_chunk_fwd_noalloc(const kda_desc *desc, const void *q, const void *k, const void *v,
                                  const float *raw_gate, const float *beta_logits, const float *a_log,
@@ -158,9 +158,10 @@ kda_status kda_chunk_fwd_noalloc(const kda_desc *desc, const void *q, const void
                                  const int32_t *state_indices, void *out, void *stream);
 
 /*
- * kda_chunk_fwd with a caller-owned workspace.  For bf16 with the safe gate
- * (bound >= -5.3, dk = dv in {64, 128}) the forward pass is load-balanced over
- * the GPU's compute units: a sequence
+ * kda_chunk_fwd with a caller-owned workspace.  For bf16 inputs (dk = dv in
+ * {64, 128}, either gate: the fast kernels with the safe gate, the chunk walk
+ * otherwise) the forward pass is load-balanced over the GPU's compute units: a
+ * sequence
  * much longer than the average load per CU is cut into pieces at chunk
  * boundaries that run in parallel, using the segment maps of KDA Context
  * Parallelism (Theory: a piece started from state X ends in M X + U, and its
@@ -173,8 +174,7 @@ kda_status kda_chunk_fwd_noalloc(const kda_desc *desc, const void *q, const void
  *                   NULL (or workspace_bytes == 0): no load balancing, one
  *                   workgroup per (sequence, head), no workspace.
  * Other arguments as for kda_chunk_fwd.  KDA_ERR_SHAPE if workspace is given
- * but smaller than required.  For other dtypes and dims the workspace is not
- * used.
+ * but smaller than required.  For f32 inputs the workspace is not used.
  */
 kda_status kda_chunk_fwd_ws(const kda_desc *desc, const void *q, const void *k, const void *v,
                             const float *raw_gate, const float *beta_logits, const float *a_log,

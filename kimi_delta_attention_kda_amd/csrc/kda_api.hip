@@ -107,10 +107,15 @@ hipMemPool_t device_pool(int dev) {
     return pools[dev];
 }
 
-bool planned_applies(const kda_desc *d) { return use_fast(d) && d->batch > 0 && d->total_tokens > 0; }
+// The load-balanced pass serves bf16 inputs (its correction rows and outputs are bf16) with
+// either gate: the fast kernels with the safe gate, the precise walk otherwise.
+bool planned_applies(const kda_desc *d) {
+    return d->qkv_dtype == KDA_BF16 && d->dk == d->dv && (d->dk == 128 || d->dk == 64) && d->batch > 0 &&
+           d->total_tokens > 0;
+}
 
 // chunk kernel of the bf16 forward pass (dk = dv in {64, 128})
-const kda::FwdKernel &fwd_kernel() { return kda::FWD64; }
+const kda::FwdKernel &fwd_kernel(const kda_desc *d) { return use_fast(d) ? kda::FWD64 : kda::FWD64_PRECISE; }
 
 kda_status workspace_bytes_for(const kda_desc *d, size_t *bytes, kda::PlanLayout *lay, int *n_cu) {
     *bytes = 0;
@@ -118,7 +123,7 @@ kda_status workspace_bytes_for(const kda_desc *d, size_t *bytes, kda::PlanLayout
     int dev = 0;
     const int cus = current_device_cus(&dev);
     if (cus <= 0) return KDA_ERR_HIP;
-    *lay = kda::plan_layout(d->total_tokens, d->batch, d->num_heads, d->dk, d->dv, fwd_kernel().per_cu * cus);
+    *lay = kda::plan_layout(d->total_tokens, d->batch, d->num_heads, d->dk, d->dv, fwd_kernel(d).per_cu * cus);
     *bytes = lay->total;
     *n_cu = cus;
     return KDA_OK;
@@ -215,22 +220,23 @@ kda_status chunk_fwd_impl(const kda_desc *desc, const void *q, const void *k, co
     a.out = out;
     a.n_items = desc->batch;
     hipError_t e;
-    if (use_fast(desc)) {
+    if (planned_applies(desc) && scratch) {
         a.n_slices = 1;
-        if (scratch) {
-            e = kda::launch_planned_fwd(a, desc->dk, scratch, *scratch_lay, scratch_ncu, fwd_kernel(),
-                                        (hipStream_t)stream);
-        } else if (workspace && workspace_bytes > 0) {
-            size_t need = 0;
-            kda::PlanLayout lay;
-            int n_cu = 0;
-            st = workspace_bytes_for(desc, &need, &lay, &n_cu);
-            if (st != KDA_OK) return st;
-            if (workspace_bytes < need) return KDA_ERR_SHAPE;
-            e = kda::launch_planned_fwd(a, desc->dk, (char *)workspace, lay, n_cu, fwd_kernel(), (hipStream_t)stream);
-        } else {
-            e = kda::launch_fast(a, desc->dk, kda::MODE_FWD, (hipStream_t)stream);
-        }
+        e = kda::launch_planned_fwd(a, desc->dk, scratch, *scratch_lay, scratch_ncu, fwd_kernel(desc),
+                                    (hipStream_t)stream);
+    } else if (planned_applies(desc) && workspace && workspace_bytes > 0) {
+        a.n_slices = 1;
+        size_t need = 0;
+        kda::PlanLayout lay;
+        int n_cu = 0;
+        st = workspace_bytes_for(desc, &need, &lay, &n_cu);
+        if (st != KDA_OK) return st;
+        if (workspace_bytes < need) return KDA_ERR_SHAPE;
+        e = kda::launch_planned_fwd(a, desc->dk, (char *)workspace, lay, n_cu, fwd_kernel(desc),
+                                    (hipStream_t)stream);
+    } else if (use_fast(desc)) {
+        a.n_slices = 1;
+        e = kda::launch_fast(a, desc->dk, kda::MODE_FWD, (hipStream_t)stream);
     } else {
         e = kda::launch_chain(a, desc->dk, desc->qkv_dtype == KDA_BF16, kda::MODE_FWD, (hipStream_t)stream);
     }
@@ -330,7 +336,7 @@ kda_status kda_chunk_fwd_noalloc(const kda_desc *desc, const void *q, const void
     if (cus <= 0) return KDA_ERR_HIP;
     bool fits = false;
     const kda::PlanLayout lay = kda::plan_layout(desc->total_tokens, desc->batch, desc->num_heads, desc->dk,
-                                                 desc->dv, fwd_kernel().per_cu * cus, SCRATCH_BYTES, &fits);
+                                                 desc->dv, fwd_kernel(desc).per_cu * cus, SCRATCH_BYTES, &fits);
     if (!fits) return KDA_ERR_SCRATCH;
     char *ws = scratch_ptr(dev);
     if (!ws) return KDA_ERR_HIP;

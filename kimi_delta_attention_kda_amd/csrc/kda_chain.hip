@@ -137,8 +137,15 @@ __device__ __forceinline__ f32x4 mma3x16(f32x4 acc, bf16x4 ah, bf16x4 al, bf16x4
     return mfma16(al, bh, acc);
 }
 
+// One unit of the chunk walk: chunks t_begin .. t_end of (item, head h), state column slice
+// `slice`.  Forward pass: the state starts from fin (init 0; V_FIRST if fin_vfirst), the identity
+// (init 1, a transition chain) or zero (init 2); values are read when v_on; output rows go to
+// obase with row 0 at token orow; the final state goes to fin.
 template <int DK, int DVS, bool IN16, int MODE>
-__global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
+__device__ __forceinline__ void chain_unit(const ChainArgs &a, char *smem, const int item, const int h,
+                                           const int t_begin, const int t_end, const int slice, const int init,
+                                           const bool v_on, const bool fin_vfirst, float *fin, void *obase,
+                                           const int64_t orow) {
     using L = Lds<DK, DVS, MODE>;
     constexpr bool FW = (MODE == MODE_FWD);
     constexpr int DV = DK;           // equal head dims
@@ -146,27 +153,15 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
     constexpr int NCT = DK / 16;     // 16-row key tiles of the state
     constexpr int NKB = DK / 32;     // 32-wide k blocks over the key dim
     constexpr int PF = L::PF, PKF = L::PKF;
-    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
-
-    // ---- work item: XCD-aware order keeps the slices of one (item, head) on one XCD
     const int H = a.H;
-    const int n_units = a.n_items * H;
-    const int lin = blockIdx.x;
-    const int xcd = lin & 7, jx = lin >> 3;
-    const int slice = jx % a.n_slices;
-    const int unit = (jx / a.n_slices) * 8 + xcd;
-    if (unit >= n_units) return;
-    const int item = unit / H, h = unit - item * H;
     const int hk = h / (H / a.Hk);  // key head of value head h
-    const int t_begin = a.offsets[item], t_end = a.offsets[item + 1];
     const int len = t_end - t_begin;
-    if (FW && len <= 0) return;  // empty sequence: slot untouched, no rows
     const int n_chunks = len > 0 ? (len + CH - 1) / CH : 0;
 
     const int aug0 = slice * DVS;            // first state column of this slice
     const bool isM = (!FW) && aug0 < DK;     // summary: transition-matrix columns
     const int col0 = (FW || isM) ? aug0 : aug0 - DK;
-    const bool has_v = FW || !isM;
+    const bool has_v = FW ? v_on : !isM;
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
     const int safe = a.gate_mode == 1;
@@ -175,8 +170,6 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 
     // ---- state slice: S[m][ct] holds rows 16ct+4g+s, column col0 + 16(w*NVT+m) + li
     f32x4 S[NVT][NCT];
-    int slot = 0;
-    if (FW) slot = a.state_indices[item];
 #pragma unroll
     for (int m = 0; m < NVT; ++m) {
         const int col = col0 + 16 * (w * NVT + m) + li;
@@ -187,8 +180,8 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                 const int c = 16 * ct + 4 * g + s;
                 float val;
                 if (FW)
-                    val = a.state_pool[a.v_first ? (((int64_t)slot * H + h) * DV + col) * DK + c
-                                                  : (((int64_t)slot * H + h) * DK + c) * DV + col];
+                    val = init == 0 ? fin[fin_vfirst ? col * DK + c : c * DV + col]
+                                    : ((init == 1 && c == col) ? 1.f : 0.f);
                 else
                     val = (isM && c == col) ? 1.f : 0.f;
                 S[m][ct][s] = val;
@@ -666,6 +659,9 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
                     vv = *(const f32x4 *)(sVT + vcol * PF + 16 * rt + 4 * g);
                 }
                 const f32x4 bb = *(const f32x4 *)(sBeta + 16 * rt + 4 * g);
+                // a transition chain has no values (its rows were read anyway, unconditionally)
+                if constexpr (L::VG)
+                    if (!has_v) vv = f32x4{0.f, 0.f, 0.f, 0.f};
                 R[m][rt] = bb * (vv - Y[m][rt]);
             }
         }
@@ -713,7 +709,7 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
                         const int i = 16 * rt + 4 * g + s;
-                        if (i < n) st_out<IN16>(a.out, ((int64_t)(t0 + i) * H + h) * DV + col, a.scale * Z[m][rt][s]);
+                        if (i < n) st_out<IN16>(obase, ((t0 - orow + i) * H + h) * DV + col, a.scale * Z[m][rt][s]);
                     }
                 }
             }
@@ -765,13 +761,79 @@ __global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
             for (int s = 0; s < 4; ++s) {
                 const int c = 16 * ct + 4 * g + s;
                 if (FW)
-                    a.state_pool[a.v_first ? (((int64_t)slot * H + h) * DV + col) * DK + c
-                                         : (((int64_t)slot * H + h) * DK + c) * DV + col] = S[m][ct][s];
+                    fin[fin_vfirst ? col * DK + c : c * DV + col] = S[m][ct][s];
                 else if (isM)
                     a.M[(((int64_t)item * H + h) * DK + c) * DK + col] = S[m][ct][s];
                 else
                     a.U[(((int64_t)item * H + h) * DK + c) * DV + col] = S[m][ct][s];
             }
+    }
+}
+
+template <int DK, int DVS, bool IN16, int MODE>
+__global__ __launch_bounds__(NT, 1) void kda_chain_kernel(ChainArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[Lds<DK, DVS, MODE>::BYTES];
+    constexpr bool FW = (MODE == MODE_FWD);
+    const int H = a.H;
+    // ---- work item: XCD-aware order keeps the slices of one (item, head) on one XCD
+    const int n_units = a.n_items * H;
+    const int lin = blockIdx.x;
+    const int xcd = lin & 7, jx = lin >> 3;
+    const int slice = jx % a.n_slices;
+    const int unit = (jx / a.n_slices) * 8 + xcd;
+    if (unit >= n_units) return;
+    const int item = unit / H, h = unit - item * H;
+    const int t_begin = a.offsets[item], t_end = a.offsets[item + 1];
+    if (FW && t_end <= t_begin) return;  // empty sequence: slot untouched, no rows
+    float *fin = FW ? a.state_pool + ((int64_t)a.state_indices[item] * H + h) * DK * DK : nullptr;
+    chain_unit<DK, DVS, IN16, MODE>(a, smem, item, h, t_begin, t_end, slice, 0, true, a.v_first, fin, a.out, 0);
+}
+
+// The forward pass of a load-balanced plan (bf16 inputs): persistent workgroups take the
+// planner's queued units (whole sequences, and the transition and contribution chains of
+// later pieces) until the queue is drained.
+template <int DK>
+__global__ __launch_bounds__(NT, 1) void kda_chain_planned_kernel(ChainArgs a) {
+    __shared__ __attribute__((aligned(16))) char smem[Lds<DK, DK, MODE_FWD>::BYTES];
+    __shared__ int s_next;
+    const int H = a.H;
+    for (;;) {
+        if (threadIdx.x == 0) s_next = atomicAdd((int *)&a.plan->ctr, 1);
+        __syncthreads();
+        const int u = __builtin_amdgcn_readfirstlane(s_next);
+        __syncthreads();
+        if (u >= a.plan->qlen) break;
+        const int2 qe = a.queue[u];
+        const int qx = __builtin_amdgcn_readfirstlane(qe.x), qy = __builtin_amdgcn_readfirstlane(qe.y);
+        if (qy < 0) continue;  // skip slot
+        const int4 en = a.ent[qx];
+        const int seq = __builtin_amdgcn_readfirstlane(en.x), cbeg = __builtin_amdgcn_readfirstlane(en.y);
+        const int cend = __builtin_amdgcn_readfirstlane(en.z), piece = __builtin_amdgcn_readfirstlane(en.w);
+        const int h = qy & 0xffff, role = qy >> 16;
+        const int sb = a.offsets[seq], se = a.offsets[seq + 1];
+        const int t_begin = sb + CH * cbeg, t_end = min(se, sb + CH * cend);
+        if (t_end <= t_begin) continue;
+        // whole sequence: from and to its slot; transition chain of a later piece: from the
+        // identity, no values, its outputs the piece's correction rows; contribution chain:
+        // from zero
+        int init = 0;
+        bool v_on = true, vf = a.v_first;
+        float *fin = a.state_pool + ((int64_t)a.state_indices[seq] * H + h) * DK * DK;
+        void *obase = a.out;
+        int64_t orow = 0;
+        if (role == ROLE_M) {
+            init = 1;
+            v_on = false;
+            vf = false;
+            fin = a.ws_M + ((int64_t)piece * H + h) * DK * DK;
+            obase = a.ws_W;
+            orow = t_begin - CH * (int64_t)__builtin_amdgcn_readfirstlane(a.ws_piece[piece].w);
+        } else if (role == ROLE_U) {
+            init = 2;
+            vf = false;
+            fin = a.ws_U + ((int64_t)piece * H + h) * DK * DK;
+        }
+        chain_unit<DK, DK, true, MODE_FWD>(a, smem, seq, h, t_begin, t_end, 0, init, v_on, vf, fin, obase, orow);
     }
 }
 
@@ -794,6 +856,21 @@ static hipError_t launch_dk(const ChainArgs &a, int dk, hipStream_t stream) {
     if (dk == 128) return launch_one<128, 128, IN16, MODE>(a, stream);
     if (dk == 64) return launch_one<64, 64, IN16, MODE>(a, stream);
     return hipErrorInvalidValue;
+}
+
+// The forward pass of a load-balanced plan on bf16 inputs: persistent workgroups (one per
+// CU) take the planner's queued units (whole sequences, and the transition and contribution
+// chains of later pieces).
+hipError_t launch_chain_planned(const ChainArgs &a0, int dk, int n_wg, hipStream_t stream) {
+    ChainArgs a = a0;
+    a.n_slices = 1;
+    if (dk == 128)
+        hipLaunchKernelGGL(kda_chain_planned_kernel<128>, dim3(n_wg), dim3(NT), 0, stream, a);
+    else if (dk == 64)
+        hipLaunchKernelGGL(kda_chain_planned_kernel<64>, dim3(n_wg), dim3(NT), 0, stream, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_chain(const ChainArgs &a, int dk, bool bf16_in, int mode, hipStream_t stream) {

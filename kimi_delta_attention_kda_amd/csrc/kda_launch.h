@@ -79,6 +79,9 @@ struct ChainArgs {
 // Precise chunk walk (kda_chain.hip): dk = dv in {64, 128}; the launch sets a.n_slices
 // (column slices per item and head) itself.  bf16_in: q/k/v (and out) are bf16, else fp32.
 hipError_t launch_chain(const ChainArgs &a, int dk, bool bf16_in, int mode, hipStream_t stream);
+// the precise walk's forward pass over the queues of a plan (a.plan set, bf16 inputs), n_wg
+// persistent workgroups
+hipError_t launch_chain_planned(const ChainArgs &a, int dk, int n_wg, hipStream_t stream);
 
 // bf16 inputs, dk = dv in {64, 128}, safe gate: dv/16-wave kernel, one workgroup per (item, head)
 // for the forward pass (n_slices = 1) and two (transition / contribution columns) for
@@ -90,17 +93,20 @@ hipError_t launch_fast_planned(const ChainArgs &a, int dk, int n_cu, hipStream_t
 // chunk apart; grid as for launch_fast (one workgroup per (item, head), or persistent
 // over a plan's queue).
 hipError_t launch_pipe(const ChainArgs &a, dim3 grid, hipStream_t stream);
-// The chunk kernel of the bf16 forward pass: its chunk length and how many of its
-// workgroups share a CU (the planner sizes pieces in its chunks, for that many slots).
-// LDS admits one workgroup per CU at dk = 128 (155 KB) and at dk = 64 (92 KB).
+// The chunk kernel of the bf16 forward pass: its chunk length, how many of its workgroups
+// share a CU (the planner sizes pieces in its chunks, for that many slots), and whether it
+// is the precise walk.  LDS admits one workgroup per CU for each of them.
 struct FwdKernel {
     int chunk;
     int per_cu;
+    bool precise;
 };
-constexpr FwdKernel FWD64 = {64, 1};  // kda_fast.hip
+constexpr FwdKernel FWD64 = {64, 1, false};         // kda_pipe.hip / kda_fast.hip (safe gate)
+constexpr FwdKernel FWD64_PRECISE = {64, 1, true};  // kda_chain.hip (other gates)
 
 // Planner, piece-state scan and output correction of the load-balanced forward pass
-// (bf16, dk = dv in {64, 128}).  ws is the workspace laid out by plan_layout.
+// (bf16, dk = dv in {64, 128}, either gate; fk names the chunk kernel).  ws is the
+// workspace laid out by plan_layout.
 hipError_t launch_planned_fwd(ChainArgs a, int dk, char *ws, const PlanLayout &lay, int n_cu,
                               const FwdKernel &fk, hipStream_t stream);
 

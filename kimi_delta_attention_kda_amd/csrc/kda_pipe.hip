@@ -396,10 +396,12 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                 }
                 __syncthreads();
 
-                // ---- second interval: O^T = S^T Qbar^T + U^T P^T, S <- e^{G_last} S + Khat^T U
+                // ---- second interval: O^T = S^T Qbar^T + U^T P^T (Qbar and P carry the query
+                // scale), S <- e^{G_last} S + Khat^T U
                 {
                     const Lane lm = lane_ids();
-                    const float osc = a.scale * iusc;
+                    // Qbar and P arrive multiplied by the query scale (in the producer), so the
+                    // output needs no multiplier unless R was rescaled
                     bf16x8 Sb[4][NCC];
 #pragma unroll
                     for (int kb = 0; kb < 4; ++kb)
@@ -427,17 +429,25 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                             for (int cc = 0; cc < NCC; ++cc)
                                 Z[cc] = mfma32h(Uh[jb][cc], pf, Z[cc]);
                         }
+                        if (usc != 1.f)
+#pragma unroll
+                            for (int cc = 0; cc < NCC; ++cc) Z[cc] *= iusc;
                         // lane holds O[token 16 rt + li][columns 32 cw + 16 cc + 4g .. +3]
                         const int i = 16 * rt + lm.li;
                         if (i < n) {
                             bf16_t *op = obase + ((t0 - orow) * H + h) * DV + (unsigned)(i * (H * DV) + 16 * NCC * cw + 4 * lm.g);
 #pragma unroll
-                            for (int cc = 0; cc < NCC; ++cc) *(bf16x4 *)(op + 16 * cc) = bf4(osc * Z[cc]);
+                            for (int cc = 0; cc < NCC; ++cc) *(bf16x4 *)(op + 16 * cc) = bf4(Z[cc]);
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     f16x8 kh[2], khn[2];
                     f32x4 e4 = *(const f32x4 *)(eg + key_row(0, 4 * lm.g)), e4n;
+                    if (usc != 1.f)
+#pragma unroll
+                        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                            for (int cc = 0; cc < NCC; ++cc) S[ct][cc] *= usc;
 #pragma unroll
                     for (int jb = 0; jb < 2; ++jb) kh[jb] = fragA_perm_h(sKH, PJ, lm.li, 32 * jb, lm.g);
 #pragma unroll
@@ -448,7 +458,7 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                             for (int jb = 0; jb < 2; ++jb) khn[jb] = fragA_perm_h(sKH, PJ, 16 * ct + 16 + lm.li, 32 * jb, lm.g);
                         }
 #pragma unroll
-                        for (int cc = 0; cc < NCC; ++cc) S[ct][cc] *= usc * e4;
+                        for (int cc = 0; cc < NCC; ++cc) S[ct][cc] *= e4;
 #pragma unroll
                         for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
@@ -691,7 +701,7 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
                         const float av = sBetaP[i] * accA[s];
                         at[s] = (li < ri) ? av : 0.f;
                         if (bI != bJ) sAO[i * PJ + j] = (f16_t)(-av);
-                        ph[pp][s] = (f16_t)((j <= i) ? accP[s] : 0.f);
+                        ph[pp][s] = (f16_t)((j <= i) ? a.scale * accP[s] : 0.f);
                     }
                     if (bI == bJ) *(f32x4 *)(sAD + (bI * 16 + li) * 20 + 4 * g) = at;
                 }
@@ -720,11 +730,12 @@ __global__ __launch_bounds__(NT, 1) void kda_pipe_kernel(ChainArgs a) {
             auto store_second = [&](const Lane &ln) {
                 const int c0 = ch0 + 4 * ln.cq, rbase = 16 * pI + 4 * ln.rq;
                 {
-                    // Qbar = Q e^{G} (Qr times the earlier blocks' decays),
+                    // Qbar = scale Q e^{G} (Qr times the earlier blocks' decays),
                     // Khat_j = K_j e^{G_last - G_j} (Kc times the later blocks' decays)
                     const f32x4 fI = decay_before(sE, c0, pI), qS = decay_after(sE, c0, pI);
+                    const f32x4 fIs = fI * a.scale;  // with the query scale
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) *(bf16x4 *)(sQB + (rbase + r) * PK + c0) = bf4(qr[r] * fI);
+                    for (int r = 0; r < 4; ++r) *(bf16x4 *)(sQB + (rbase + r) * PK + c0) = bf4(qr[r] * fIs);
 #pragma unroll
                     for (int cc = 0; cc < 4; ++cc)
                         *(f16x4 *)(sKH + tile_row(c0 + cc) * PJ + rbase) =

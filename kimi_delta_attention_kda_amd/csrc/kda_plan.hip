@@ -665,7 +665,8 @@ hipError_t launch_planned_fwd(ChainArgs a, int dk, char *ws, const PlanLayout &l
     a.ws_U = (float *)(ws + lay.U);
     a.ws_W = ws + lay.W;
     a.ws_piece = pa.piece;
-    e = launch_fast_planned(a, dk, fk.per_cu * n_cu, stream);
+    e = fk.precise ? launch_chain_planned(a, dk, fk.per_cu * n_cu, stream)
+                   : launch_fast_planned(a, dk, fk.per_cu * n_cu, stream);
     if (e != hipSuccess) return e;
 
     plan::PieceArgs pp;

@@ -37,7 +37,8 @@ def _n_slots():
 
 def _desc(w, inp):
     return kda.make_desc(w.T, w.B, w.H, w.dk, w.dv, inp["state_pool"].shape[0], torch.bfloat16,
-                         torch.bfloat16, "safe", w.lower_bound, "logits", "K_FIRST", w.scale)
+                         torch.bfloat16, "safe" if w.gate_mode == 1 else "original", w.lower_bound, "logits",
+                         "K_FIRST", w.scale)
 
 
 def _run_with_ws(w, inp, nbytes=None):
@@ -98,6 +99,24 @@ def test_many_pieces_against_oracle(lengths, dk):
     from kda_testlib import untouched_slots_identical
     w = wl.custom(lengths, H=2, dk=dk, dv=dk, name="pieces")
     print(f"[case] pieces lengths={lengths} H=2 dk={dk}", flush=True)
+    inp = wl.make_inputs(w, "cuda")
+    st, out, pool, hdr = _run_with_ws(w, inp)
+    assert st == 0
+    _check_plan(w, hdr)
+    assert _header(hdr)["n_piece"] >= 4
+    assert untouched_slots_identical(inp, pool)
+    _compare_all(w, inp, out, pool)
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_original_gate_pieces_against_oracle(dk):
+    """bf16 with the original gate runs the precise walk over the same plan: the later
+    pieces as transition and contribution chains, then the piece-state scan and the
+    correction."""
+    from kda_testlib import untouched_slots_identical
+    lengths = (3000, 100, 5000, 0, 64, 777)
+    w = wl.custom(lengths, H=2, dk=dk, dv=dk, gate_mode=0, name="pieces_original_gate", seed=5)
+    print(f"[case] original gate, pieces lengths={lengths} H=2 dk={dk}", flush=True)
     inp = wl.make_inputs(w, "cuda")
     st, out, pool, hdr = _run_with_ws(w, inp)
     assert st == 0

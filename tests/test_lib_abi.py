@@ -144,15 +144,14 @@ def test_workspace_variant_error_paths(L):
     assert L.kda_chunk_fwd_workspace_size(C.byref(_desc(qkv_dtype=torch.float32, out_dtype=torch.float32,
                                                          dk=64, dv=64)), C.byref(n)) == OK
     assert n.value == 0
-    # neither does the precise walk (bf16 with the original gate)
-    assert L.kda_chunk_fwd_workspace_size(C.byref(_desc(gate_mode="original")), C.byref(n)) == OK
-    assert n.value == 0
-    # bf16 with the safe gate sizes for the current device (HIP error without one)
-    for dk in (128, 64):
-        st = L.kda_chunk_fwd_workspace_size(C.byref(_desc(dk=dk, dv=dk)), C.byref(n))
-        assert st in (OK, 6)
-        if st == OK:
-            assert n.value >= 128 * 4 * dk * 2
+    # bf16 with either gate (the fast kernels, or the precise walk for the original gate)
+    # sizes for the current device (HIP error without one)
+    for gate in ("safe", "original"):
+        for dk in (128, 64):
+            st = L.kda_chunk_fwd_workspace_size(C.byref(_desc(dk=dk, dv=dk, gate_mode=gate)), C.byref(n))
+            assert st in (OK, 6)
+            if st == OK:
+                assert n.value >= 128 * 4 * dk * 2
 
 
 def _fwd_noalloc(L, d, **ptrs):
