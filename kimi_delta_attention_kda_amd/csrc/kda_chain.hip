@@ -157,6 +157,11 @@ __device__ __forceinline__ void chain_unit(const ChainArgs &a, char *smem, const
     const int hk = h / (H / a.Hk);  // key head of value head h
     const int len = t_end - t_begin;
     const int n_chunks = len > 0 ? (len + CH - 1) / CH : 0;
+    // The forward pass on bf16 inputs needs bf16-level results only: the scores and the
+    // output's products (Qbar S, P U) take both operands unsplit, Y = Kg S splits only S (the
+    // state's own rounding is what accumulates), and the solve and the state update keep
+    // every split; fp32 inputs and the summaries keep every three-way split.
+    constexpr bool LITE = FW && IN16;
 
     const int aug0 = slice * DVS;            // first state column of this slice
     const bool isM = (!FW) && aug0 < DK;     // summary: transition-matrix columns
@@ -510,8 +515,8 @@ __device__ __forceinline__ void chain_unit(const ChainArgs &a, char *smem, const
                         for (int s = 0; s < 8; ++s) kj[s] *= __expf(gr[s] - gj[s]);
                         bf16x8 jh, jl;
                         split8(kj, jh, jl);
-                        oA[o] = mma3(oA[o], kh, kl, jh, jl, true, true);
-                        if (FW) oP[o] = mma3(oP[o], qh, ql, jh, jl, true, true);
+                        oA[o] = mma3(oA[o], kh, kl, jh, jl, !LITE, !LITE);
+                        if (FW) oP[o] = mma3(oP[o], qh, ql, jh, jl, !LITE, !LITE);
                     }
                 }
 #pragma unroll
@@ -625,12 +630,12 @@ __device__ __forceinline__ void chain_unit(const ChainArgs &a, char *smem, const
                 bf16x8 ah, alo;
                 split8(xk, ah, alo);
 #pragma unroll
-                for (int m = 0; m < NVT; ++m) Y[m][rt] = mma3(Y[m][rt], ah, alo, Sh[m][kb], Sl[m][kb], true, true);
+                for (int m = 0; m < NVT; ++m) Y[m][rt] = mma3(Y[m][rt], ah, alo, Sh[m][kb], Sl[m][kb], !LITE, true);
                 if (FW) {
                     split8(xq, ah, alo);
 #pragma unroll
                     for (int m = 0; m < NVT; ++m)
-                        Z[m][rt] = mma3(Z[m][rt], ah, alo, Sh[m][kb], Sl[m][kb], true, true);
+                        Z[m][rt] = mma3(Z[m][rt], ah, alo, Sh[m][kb], Sl[m][kb], !LITE, !LITE);
                 }
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
@@ -701,7 +706,7 @@ __device__ __forceinline__ void chain_unit(const ChainArgs &a, char *smem, const
 #pragma unroll
                     for (int m = 0; m < NVT; ++m)
                         Z[m][rt] = mma3(Z[m][rt], ah, alo, cat(Uh[m][2 * jb], Uh[m][2 * jb + 1]),
-                                        cat(Ul[m][2 * jb], Ul[m][2 * jb + 1]), true, true);
+                                        cat(Ul[m][2 * jb], Ul[m][2 * jb + 1]), !LITE, !LITE);
                 }
 #pragma unroll
                 for (int m = 0; m < NVT; ++m) {
