@@ -31,14 +31,16 @@ def _both(w, inp):
     return out_s, pool_s, out_t, pool_t
 
 
-@pytest.mark.parametrize("dk", [128, 64])
-def test_noalloc_matches_the_workspace_entry_point_on_two_calls(dk):
+@pytest.mark.parametrize("dk,gate", [(128, 1), (64, 1), (128, 0)])
+def test_noalloc_matches_the_workspace_entry_point_on_two_calls(dk, gate):
+    """gate 1: the safe gate (fast kernels); gate 0: the original gate (the chunk walk over
+    the same plan)."""
     from kda_testlib import compare_items, untouched_slots_identical, report, OUT_TOL_BF16, STATE_TOL
-    first = wl.custom([5000, 300, 2000, 64, 0, 1500, 700], H=2, dk=dk, dv=dk, dtype="bf16", gate_mode=1,
+    first = wl.custom([5000, 300, 2000, 64, 0, 1500, 700], H=2, dk=dk, dv=dk, dtype="bf16", gate_mode=gate,
                       n_slots=12, seed=31)
-    second = wl.custom([1200, 77, 640], H=2, dk=dk, dv=dk, dtype="bf16", gate_mode=1, n_slots=5, seed=32)
+    second = wl.custom([1200, 77, 640], H=2, dk=dk, dv=dk, dtype="bf16", gate_mode=gate, n_slots=5, seed=32)
     for w in (first, second):
-        print(f"[case] noalloc dk={dk} lengths={w.lengths}", flush=True)
+        print(f"[case] noalloc dk={dk} gate_mode={gate} lengths={w.lengths}", flush=True)
         inp = wl.make_inputs(w, "cuda")
         out_s, pool_s, out_t, pool_t = _both(w, inp)
         assert torch.equal(out_s.view(torch.int16), out_t.view(torch.int16))
@@ -46,7 +48,7 @@ def test_noalloc_matches_the_workspace_entry_point_on_two_calls(dk):
         assert untouched_slots_identical(inp, pool_s)
         items = [(b, h) for b in range(w.B) for h in range(w.H)]
         eo, es = compare_items(w, inp, out_s, pool_s, items)
-        report(f"no-alloc entry point, dk={dk}, lengths {w.lengths}: bit-identical to the workspace "
+        report(f"no-alloc entry point, dk={dk}, gate_mode={gate}, lengths {w.lengths}: bit-identical to the workspace "
                f"entry point; oracle out_err={eo:.3e} state_err={es:.3e}")
         assert eo <= OUT_TOL_BF16 and es <= STATE_TOL
 
