@@ -48,10 +48,11 @@ def measured_traffic(w):
 
 
 def chunk_kernel(w) -> str:
-    """The chunk kernel that kda_chunk_fwd runs for workload w."""
+    """The chunk kernel that kda_chunk_fwd runs for workload w (with its load-balancing
+    workspace, as bench.py calls it)."""
     if w.dtype == "bf16" and w.gate_mode == 1 and w.lower_bound >= -5.3:
         return "kda_pipe_kernel" if w.dk == 128 else "kda_fast_kernel"
-    return "kda_chain_kernel"
+    return "kda_chain_planned_kernel" if w.dtype == "bf16" else "kda_chain_kernel"
 
 
 def measured_utilization(w, kernel=None):
@@ -494,8 +495,9 @@ def run_segments(args, w):
                                + ("kda_affine_scan_mfma" if w.dk in (64, 128) else "kda_affine_scan_kernel"),
                      "kernel_ms": round(kern_ms, 4),
                      "algorithmic_bytes_per_launch": nbytes,
-                     "profiled_busy": measured_utilization(w, chunk_kernel(w) if chunk_kernel(w) == "kda_chain_kernel"
-                                                           else "kda_fast_kernel")},
+                     "profiled_busy": measured_utilization(
+                         w, "kda_fast_kernel" if w.dtype == "bf16" and w.gate_mode == 1 and w.lower_bound >= -5.3
+                         else "kda_chain_kernel")},
         "per_call": protocol,
         "cpu_baseline": cpu,
     }
