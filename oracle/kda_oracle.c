@@ -30,6 +30,8 @@
  *   Exclusive scan (KDA Context Parallelism, "Incoming and outgoing states" and
  *   "Implementation order"): W = S_init; for each segment in order: record W as
  *   incoming, W = M_i W + U_i, record W as outgoing; final = W.
+ *   Composition of two maps (the same page, "Theory" and "A scalar three-segment
+ *   example"): F2 after F1 is S -> M2 (M1 S + U1) + U2 = (M2 M1) S + (M2 U1 + U2).
  *
  * All arrays are row-major, contiguous, double precision.
  */
@@ -226,6 +228,28 @@ void kda_ref_segment_map(const kda_ref_item *it, int dk, int dv, int gate_mode, 
 }
 
 /* ---------------------------------------------------------------- scan -- */
+
+/*
+ * Composition of two segment maps, F1 applied first, then F2:
+ *   Mo = M2 M1,  Uo = M2 U1 + U2.
+ * M1, M2 [dk,dk], U1, U2 [dk,dv] -> Mo [dk,dk], Uo [dk,dv].  The outputs must not
+ * alias the inputs.
+ */
+void kda_ref_compose(int dk, int dv, const double *M2, const double *U2, const double *M1,
+                     const double *U1, double *Mo, double *Uo) {
+    for (int i = 0; i < dk; ++i) {
+        for (int j = 0; j < dk; ++j) {
+            double acc = 0.0;
+            for (int c = 0; c < dk; ++c) acc += M2[i * dk + c] * M1[c * dk + j];
+            Mo[i * dk + j] = acc;
+        }
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int c = 0; c < dk; ++c) acc += M2[i * dk + c] * U1[c * dv + j];
+            Uo[i * dv + j] = acc + U2[i * dv + j];
+        }
+    }
+}
 
 /*
  * Ordered exclusive prefix of affine segment maps.

@@ -40,6 +40,7 @@ def lib():
                                                 C.c_int, C.c_int, C.c_int, C.c_double, C.c_int, C.c_int]
         L.kda_ref_scan.argtypes = [C.c_int, C.c_int, C.c_int, dp, dp, dp, dp, dp, dp]
         L.kda_ref_scan.restype = C.c_int
+        L.kda_ref_compose.argtypes = [C.c_int, C.c_int, dp, dp, dp, dp, dp, dp]
         _lib = L
     return _lib
 
@@ -150,6 +151,18 @@ def scan(M, U, S_init):
     if rc != 0:
         raise ValueError("at least one segment is required")
     return {"incoming_states": inc, "outgoing_states": outg, "final_state": fin}
+
+
+def compose(M2, U2, M1, U1):
+    """The map "F1, then F2" of two affine maps F(S) = M S + U of one head:
+    (M2 M1, M2 U1 + U2).  M [dk,dk], U [dk,dv] -> (M, U)."""
+    M2, U2, M1, U1 = _f64(M2), _f64(U2), _f64(M1), _f64(U1)
+    dk, dv = U1.shape
+    if M1.shape != (dk, dk) or M2.shape != (dk, dk) or U2.shape != (dk, dv):
+        raise ValueError("maps of different shapes")
+    Mo, Uo = np.zeros((dk, dk)), np.zeros((dk, dv))
+    lib().kda_ref_compose(dk, dv, _p(M2), _p(U2), _p(M1), _p(U1), _p(Mo), _p(Uo))
+    return Mo, Uo
 
 
 # ----------------------------------------------------------- from inputs --

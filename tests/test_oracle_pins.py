@@ -368,3 +368,92 @@ def test_scan_equals_composed_maps_and_exact():
     e = exact.exact_scan(M.tolist(), U.tolist(), S.tolist())
     assert np.array_equal(np.array(e["final_state"], dtype=float), r["final_state"])
     assert np.array_equal(np.array(e["incoming_states"], dtype=float), r["incoming_states"])
+
+
+# ------------------------------------------------------------- composition --
+# KDA Context Parallelism ("Theory", "A scalar three-segment example"): segment maps
+# compose, the composition is associative but not commutative, so the prefix may be
+# regrouped (a tree or blocked scan) but never reordered.
+
+def test_compose_reproduces_scalar_example():
+    g = _golden()
+    M = [np.array([[m]]) for m in g["M"]]
+    U = [np.array([[u]]) for u in g["U"]]
+    Mc, Uc = orc.compose(M[1], U[1], M[0], U[0])  # F1 after F0
+    assert [Mc[0, 0], Uc[0, 0]] == g["compose_F1_after_F0"]
+    assert Mc[0, 0] * g["S_init"] + Uc[0, 0] == g["compose_F1_after_F0_applied_to_initial"]
+    Mr, Ur = orc.compose(M[0], U[0], M[1], U[1])  # F0 after F1
+    assert [Mr[0, 0], Ur[0, 0]] == g["compose_F0_after_F1"]
+
+
+def test_compose_is_associative_not_commutative():
+    rng = np.random.default_rng(31)
+    dk, dv = 3, 2
+    F = [(rng.integers(-4, 5, size=(dk, dk)) / 4.0, rng.integers(-4, 5, size=(dk, dv)) / 4.0)
+         for _ in range(3)]
+    left = orc.compose(*F[2], *orc.compose(*F[1], *F[0]))    # F2 o (F1 o F0)
+    right = orc.compose(*orc.compose(*F[2], *F[1]), *F[0])   # (F2 o F1) o F0
+    # dyadic entries: every product and sum is exact, so the two groupings agree bitwise
+    assert np.array_equal(left[0], right[0]) and np.array_equal(left[1], right[1])
+    # and equal the exact rational product applied to any state
+    S = rng.integers(-4, 5, size=(dk, dv)) / 4.0
+    e = exact.exact_scan([f[0].tolist() for f in F], [f[1].tolist() for f in F], S.tolist())
+    assert np.array_equal(left[0] @ S + left[1], np.array(e["final_state"], dtype=float))
+    # generic maps: the groupings agree to rounding
+    dk, dv = 16, 8
+    G = [(rng.normal(size=(dk, dk)) / 4, rng.normal(size=(dk, dv))) for _ in range(3)]
+    l2 = orc.compose(*G[2], *orc.compose(*G[1], *G[0]))
+    r2 = orc.compose(*orc.compose(*G[2], *G[1]), *G[0])
+    assert np.allclose(l2[0], r2[0], rtol=1e-13, atol=1e-13)
+    assert np.allclose(l2[1], r2[1], rtol=1e-13, atol=1e-13)
+    # but not commutative: the order of segments matters
+    a, b = orc.compose(*G[1], *G[0]), orc.compose(*G[0], *G[1])
+    assert not np.allclose(a[0], b[0]) and not np.allclose(a[1], b[1])
+
+
+def _blocked_scan(M, U, S, blk):
+    """Exclusive prefix regrouped into blocks of blk segments: each block's maps composed
+    in order, the block composites scanned from S, then each block walked from its own
+    incoming state."""
+    n = M.shape[0]
+    starts = list(range(0, n, blk))
+    comps = []
+    for s0 in starts[:-1]:
+        Mc, Uc = M[s0], U[s0]
+        for s in range(s0 + 1, s0 + blk):
+            Mc, Uc = orc.compose(M[s], U[s], Mc, Uc)
+        comps.append((Mc, Uc))
+    block_in = [S]
+    if comps:
+        r = orc.scan(np.stack([c[0] for c in comps]), np.stack([c[1] for c in comps]), S)
+        block_in += list(r["outgoing_states"])
+    inc, out = [], []
+    for s0, Sb in zip(starts, block_in):
+        r = orc.scan(M[s0:s0 + blk], U[s0:s0 + blk], Sb)
+        inc += list(r["incoming_states"])
+        out += list(r["outgoing_states"])
+    return np.stack(inc), np.stack(out), r["final_state"]
+
+
+@pytest.mark.parametrize("blk", [1, 2, 3, 4, 6, 7, 9])
+def test_blocked_regrouping_equals_serial_scan(blk):
+    rng = np.random.default_rng(32 + blk)
+    n, dk, dv = 7, 4, 3
+    # dyadic maps: all groupings are exact, so the blocked scan reproduces the serial one bitwise
+    M = rng.integers(-4, 5, size=(n, dk, dk)) / 4.0
+    U = rng.integers(-4, 5, size=(n, dk, dv)) / 4.0
+    S = rng.integers(-4, 5, size=(dk, dv)) / 4.0
+    ser = orc.scan(M, U, S)
+    inc, out, fin = _blocked_scan(M, U, S, blk)
+    assert np.array_equal(inc, ser["incoming_states"])
+    assert np.array_equal(out, ser["outgoing_states"])
+    assert np.array_equal(fin, ser["final_state"])
+    # generic maps: equal to rounding
+    M = rng.normal(size=(n, dk, dk)) / 2
+    U = rng.normal(size=(n, dk, dv))
+    S = rng.normal(size=(dk, dv))
+    ser = orc.scan(M, U, S)
+    inc, out, fin = _blocked_scan(M, U, S, blk)
+    assert np.allclose(inc, ser["incoming_states"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(out, ser["outgoing_states"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(fin, ser["final_state"], rtol=1e-12, atol=1e-12)
