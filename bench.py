@@ -414,6 +414,31 @@ def run_decode(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def scan_variants(dev, H, dk, dv, counts=(16, 64, 256), reps=20):
+    """The exclusive scan alone, ordered against blocked (automatic block size), on seeded
+    random maps M = I + 0.05 N / sqrt(dk), U ~ N(0, 1) of the workload's head and state
+    shapes, for several segment counts: per-call median of HIP-event timings."""
+    import torch
+    import kimi_delta_attention_kda_amd as kda
+    g = torch.Generator(device=dev).manual_seed(11)
+    out = []
+    for n in counts:
+        M = torch.eye(dk, device=dev) + 0.05 * torch.randn(n, H, dk, dk, generator=g, device=dev) / dk ** 0.5
+        U = torch.randn(n, H, dk, dv, generator=g, device=dev)
+        S = torch.randn(H, dk, dv, generator=g, device=dev)
+        inc, outg, fin = torch.empty_like(U), torch.empty_like(U), torch.empty_like(S)
+        rec = {"segments": n, "block": kda.affine_scan_block_size(n, dk, dv, 0)}
+        for name, blk in (("ordered_ms", None), ("blocked_ms", 0)):
+            pc = per_call_protocol(lambda: kda.affine_exclusive_scan(M, U, S, inc, outg, fin, block=blk),
+                                   lambda: None, reps=reps)
+            rec[name] = pc["median_ms"]
+        out.append(rec)
+        print(f"[bench] scan alone, {n} segments x {H} heads: ordered {rec['ordered_ms']:.4f} ms, "
+              f"blocked (blocks of {rec['block']}) {rec['blocked_ms']:.4f} ms", file=sys.stderr, flush=True)
+        del M, U, S, inc, outg, fin
+    return out
+
+
 def run_segments(args, w):
     """kda_segment_summary over the workload's equal segments, then kda_affine_exclusive_scan
     of the maps from the initial state: one step of the per-segment pass of KDA Context
@@ -499,6 +524,7 @@ def run_segments(args, w):
                          w, "kda_fast_kernel" if w.dtype == "bf16" and w.gate_mode == 1 and w.lower_bound >= -5.3
                          else "kda_chain_kernel")},
         "per_call": protocol,
+        "scan_variants": scan_variants(dev, w.H, w.dk, w.dv) if w.dk in (64, 128) else None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -244,6 +244,40 @@ kda_status kda_affine_exclusive_scan(int32_t n_seg, int32_t num_heads, int32_t d
                                      void *stream);
 
 /*
+ * The same exclusive prefix, regrouped (KDA Context Parallelism, "Theory": the
+ * composition of segment maps is associative, so the ordered prefix may be
+ * grouped in any way that keeps the order).  Segments are taken in blocks of
+ * `block` consecutive segments:
+ *   1. each block's maps, but the last block's, are composed in order into one
+ *      map (A_b, B_b) = F_last o ... o F_first (a walk of the augmented state
+ *      [A | B] from [I | 0]), all blocks and heads in parallel;
+ *   2. W = S_init; W <- A_b W + B_b over the block composites in order gives
+ *      every block's incoming state;
+ *   3. each block is walked from its incoming state as in the ordered scan,
+ *      all blocks in parallel, writing incoming, outgoing and (last block) final.
+ * The critical path is about 2 block + n_seg / block map steps instead of n_seg;
+ * the work is about three times the ordered scan's.  Results equal those of
+ * kda_affine_exclusive_scan up to fp32 rounding of the regrouped products.
+ *   block: segments per block; 0 picks the ordered scan below 32 segments (where
+ *     its one launch is faster) and about sqrt(n_seg / 2) from 32 on.  It is raised to
+ *     at least 1 + ceil(dk / dv), because the block composites (dk x (dk + dv)
+ *     per block and head) are kept in `outgoing` until step 3 overwrites it;
+ *     a block of n_seg or more is the ordered scan.  kda_affine_scan_block_size
+ *     returns the block a call would use.
+ *   Arrays, layouts, dtypes and errors as kda_affine_exclusive_scan; the inputs
+ *   are read only; `outgoing` is scratch until the call completes.  dk in
+ *   {16, 32} runs the ordered scan.  Three kernel launches on `stream`.
+ */
+kda_status kda_affine_exclusive_scan_blocked(int32_t n_seg, int32_t num_heads, int32_t dk, int32_t dv,
+                                             int32_t block, const float *M, const float *U,
+                                             const float *S_init, float *incoming, float *outgoing,
+                                             float *final_state, void *stream);
+
+/* Block size kda_affine_exclusive_scan_blocked uses for these arguments (n_seg when it
+ * runs the ordered scan); -1 for invalid arguments.  Host only, no GPU call. */
+int32_t kda_affine_scan_block_size(int32_t n_seg, int32_t dk, int32_t dv, int32_t block);
+
+/*
  * Synchronous debug check of the data-dependent preconditions of
  * kda_chunk_fwd (max.nn.state_space.kda_chunk, Raises: the shape guards that
  * a production build leaves out).  cu_seqlens [batch+1] and state_indices

@@ -8,7 +8,7 @@ every call raises RuntimeError; there is no CPU fallback.
 Entry points (names as in the C ABI, include/libkda.h):
   chunk_fwd(...)          varlen chunk-parallel prefill, mutates the state pool in place
   segment_summary(...)    per-segment affine maps (M_i, U_i)
-  affine_exclusive_scan(M, U, S_init) -> (incoming, outgoing, final)
+  affine_exclusive_scan(M, U, S_init[, block]) -> (incoming, outgoing, final), ordered or blocked
   context_parallel(transition_matrices, local_contributions, initial_state) -> dict
   validate_varlen(...)    synchronous debug check of cu_seqlens / state_indices
 """
@@ -57,11 +57,15 @@ def lib():
         L.kda_decode.argtypes = [dp] + [vp] * 11
         L.kda_segment_summary.argtypes = [dp] + [vp] * 7 + [i32, vp, vp, vp]
         L.kda_affine_exclusive_scan.argtypes = [i32, i32, i32, i32] + [vp] * 7
+        L.kda_affine_exclusive_scan_blocked.argtypes = [i32, i32, i32, i32, i32] + [vp] * 7
+        L.kda_affine_scan_block_size.argtypes = [i32, i32, i32, i32]
+        L.kda_affine_scan_block_size.restype = i32
         L.kda_validate_varlen.argtypes = [vp, i32, i64, vp, i32]
         L.kda_status_string.argtypes = [C.c_int]
         L.kda_status_string.restype = C.c_char_p
         for f in ("kda_chunk_fwd", "kda_chunk_fwd_ws", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_workspace_size", "kda_decode",
-                  "kda_segment_summary", "kda_affine_exclusive_scan", "kda_validate_varlen"):
+                  "kda_segment_summary", "kda_affine_exclusive_scan", "kda_affine_exclusive_scan_blocked",
+                  "kda_validate_varlen"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -307,8 +311,21 @@ def segment_summary(k, v, raw_gate, beta_logits, a_log, dt_bias, seg_offsets, *,
     return M, U
 
 
-def affine_exclusive_scan(M, U, S_init, incoming=None, outgoing=None, final_state=None):
-    """M [n,H,dk,dk], U [n,H,dk,dv], S_init [H,dk,dv] (f32, device) -> (incoming, outgoing, final)."""
+def affine_scan_block_size(n_seg, dk, dv, block=0):
+    """Segments per block that the blocked scan uses for these arguments (n_seg: the
+    ordered scan).  Host only."""
+    b = lib().kda_affine_scan_block_size(int(n_seg), int(dk), int(dv), int(block))
+    if b < 0:
+        raise ValueError("invalid scan arguments")
+    return b
+
+
+def affine_exclusive_scan(M, U, S_init, incoming=None, outgoing=None, final_state=None, block=None):
+    """M [n,H,dk,dk], U [n,H,dk,dv], S_init [H,dk,dv] (f32, device) -> (incoming, outgoing, final).
+
+    block None: the ordered scan (kda_affine_exclusive_scan).  block >= 0: the same
+    prefix regrouped into blocks of that many segments (0: automatic), three launches
+    (kda_affine_exclusive_scan_blocked)."""
     if M.dim() != 4 or U.dim() != 4 or S_init.dim() != 3:
         raise ValueError("expected M [n,H,dk,dk], U [n,H,dk,dv], S_init [H,dk,dv]")
     n, H, dk, _ = M.shape
@@ -326,9 +343,16 @@ def affine_exclusive_scan(M, U, S_init, incoming=None, outgoing=None, final_stat
     incoming = torch.empty_like(U) if incoming is None else incoming
     outgoing = torch.empty_like(U) if outgoing is None else outgoing
     final_state = torch.empty_like(S_init) if final_state is None else final_state
-    _check(lib().kda_affine_exclusive_scan(int(n), int(H), int(dk), int(dv), _ptr(M), _ptr(U),
-                                           _ptr(S_init), _ptr(incoming), _ptr(outgoing),
-                                           _ptr(final_state), _stream()))
+    if block is None:
+        _check(lib().kda_affine_exclusive_scan(int(n), int(H), int(dk), int(dv), _ptr(M), _ptr(U),
+                                               _ptr(S_init), _ptr(incoming), _ptr(outgoing),
+                                               _ptr(final_state), _stream()))
+    else:
+        if int(block) < 0:
+            raise ValueError("block must be >= 0")
+        _check(lib().kda_affine_exclusive_scan_blocked(int(n), int(H), int(dk), int(dv), int(block), _ptr(M),
+                                                       _ptr(U), _ptr(S_init), _ptr(incoming), _ptr(outgoing),
+                                                       _ptr(final_state), _stream()))
     return incoming, outgoing, final_state
 
 

@@ -454,6 +454,24 @@ kda_status kda_affine_exclusive_scan(int32_t n_seg, int32_t num_heads, int32_t d
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_affine_exclusive_scan_blocked(int32_t n_seg, int32_t num_heads, int32_t dk, int32_t dv,
+                                             int32_t block, const float *M, const float *U,
+                                             const float *S_init, float *incoming, float *outgoing,
+                                             float *final_state, void *stream) {
+    if (n_seg < 1 || num_heads <= 0 || dk <= 0 || dv <= 0 || block < 0) return KDA_ERR_SHAPE;
+    if (!M || !U || !S_init || !incoming || !outgoing || !final_state) return KDA_ERR_NULL;
+    if (!(dk == 16 || dk == 32 || dk == 64 || dk == 128) || dv % 16 != 0) return KDA_ERR_UNSUPPORTED;
+    hipError_t e = kda::launch_affine_scan_blocked(n_seg, num_heads, dk, dv, block, M, U, S_init, incoming,
+                                                   outgoing, final_state, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int32_t kda_affine_scan_block_size(int32_t n_seg, int32_t dk, int32_t dv, int32_t block) {
+    if (n_seg < 1 || dk <= 0 || dv <= 0 || block < 0) return -1;
+    if (!(dk == 64 || dk == 128)) return n_seg;
+    return kda::scan_block_size(n_seg, dk, dv, block);
+}
+
 kda_status kda_validate_varlen(const int32_t *cu_seqlens, int32_t batch, int64_t total_tokens,
                                const int32_t *state_indices, int32_t max_slots) {
     if (batch < 0 || total_tokens < 0 || max_slots <= 0) return KDA_ERR_SHAPE;

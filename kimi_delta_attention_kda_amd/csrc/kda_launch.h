@@ -132,5 +132,13 @@ hipError_t launch_decode(const DecodeArgs &a, int dk, bool bf16, hipStream_t str
 hipError_t launch_affine_scan(int n_seg, int H, int dk, int dv, const float *M, const float *U,
                               const float *S_init, float *incoming, float *outgoing, float *final_state,
                               hipStream_t stream);
+// The same prefix regrouped into blocks of blk segments (0: about sqrt(n_seg / 2)): block
+// composites, a walk over them, then every block walked from its incoming state; three
+// launches, the composites kept in outgoing until the last overwrites it.  dk in {16, 32}
+// runs the ordered walk.
+int scan_block_size(int n_seg, int dk, int dv, int blk);
+hipError_t launch_affine_scan_blocked(int n_seg, int H, int dk, int dv, int blk, const float *M,
+                                      const float *U, const float *S_init, float *incoming,
+                                      float *outgoing, float *final_state, hipStream_t stream);
 
 }  // namespace kda

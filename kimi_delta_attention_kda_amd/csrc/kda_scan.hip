@@ -89,48 +89,101 @@ __device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
 template <int DK>
 __device__ __forceinline__ int wx_at(int k, int c) { return 16 * k + c + 16 * (k / (DK / 4)); }
 
+// What one launch of the walk does.  The composition is associative (KDA Context
+// Parallelism, "Theory"), so the ordered prefix may be regrouped into blocks of blk
+// segments:
+//   WALK_COMPOSE  task b < n_blocks - 1: the composite of block b's maps, walked on the
+//                 augmented state [A | B] = [I | 0] with maps X <- M_s X + [0 | U_s],
+//                 stored to comp[b] = [A_b | B_b] ([H, dk, dk + dv] per block);
+//   WALK_BLOCKS   one task: W = S_init, W <- A_b W + B_b for b = 0 .. n_blocks - 2, each W
+//                 stored as the incoming state of block b + 1;
+//   WALK_SEGMENTS task b: block b's segments walked from its incoming state (S_init for
+//                 block 0), incoming and outgoing stored, the last block's W as final.
+// The plain ordered walk is WALK_SEGMENTS with one block of n_seg segments.
+enum { WALK_SEGMENTS = 0, WALK_COMPOSE = 1, WALK_BLOCKS = 2 };
+struct ScanWalk {
+    int mode, n_seg, H, dv, blk, n_task;
+    int width;  // state columns walked: dv, or dk + dv for WALK_COMPOSE
+    const float *M, *U, *S_init;
+    float *incoming, *outgoing, *final_state;
+    float *comp;  // block composites (WALK_COMPOSE writes, WALK_BLOCKS reads)
+};
+
 template <int DK>
-__global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(int n_seg, int H, int dv,
-                                                                const float *__restrict__ M,
-                                                                const float *__restrict__ U,
-                                                                const float *__restrict__ S_init,
-                                                                float *incoming, float *outgoing,
-                                                                float *final_state) {
+__global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
     constexpr int TT = DK / 64, RW = DK / 4, KQ = DK / 4;
     __shared__ float sx[16 * DK + 16 * 4];
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
-    const int ncb = dv / 16;
-    const int n_lin = (H * ncb + 8 * ncb - 1) / (8 * ncb) * (8 * ncb);
+    const int H = a.H, dv = a.dv;
+    const int ncb = a.width / 16, n_hh = (H + 7) / 8;
+    const int n_lin = 8 * a.n_task * n_hh * ncb;
     for (int lin = blockIdx.x; lin < n_lin; lin += gridDim.x) {
-        // workgroups are dealt to the 8 XCDs round-robin: lin & 7 picks the XCD
-        const int cb = (lin >> 3) % ncb, h = (lin / (8 * ncb)) * 8 + (lin & 7);
+        // workgroups are dealt to the 8 XCDs round-robin: lin & 7 picks the XCD, and every
+        // column block of a head runs on the same one, so each map comes from HBM once
+        const int r = lin >> 3, cb = r % ncb, hh = (r / ncb) % n_hh, task = r / (ncb * n_hh);
+        const int h = 8 * hh + (lin & 7);
         if (h >= H) continue;  // uniform over the workgroup
         const int col = 16 * cb + li;
         auto row = [&](int tt, int s) { return RW * w + 16 * tt + 4 * g + s; };
+        // the task's maps: step i reads M rows at m0 + i m_step (row pitch ldm) and U
+        // column ucol at u0 + i u_step (row pitch ldu); no U for the identity columns
+        const int s0 = a.mode == WALK_BLOCKS ? 0 : task * a.blk;
+        const int n_steps = a.mode == WALK_BLOCKS ? (a.n_seg + a.blk - 1) / a.blk - 1 : min(a.blk, a.n_seg - s0);
+        const float *m0, *u0;
+        int64_t m_step, u_step;
+        int ldm, ldu, ucol = col;
+        bool has_u = true;
+        if (a.mode == WALK_BLOCKS) {
+            m0 = a.comp + (int64_t)h * DK * (DK + dv);
+            u0 = m0 + DK;
+            m_step = u_step = (int64_t)H * DK * (DK + dv);
+            ldm = ldu = DK + dv;
+        } else {
+            m0 = a.M + ((int64_t)s0 * H + h) * DK * DK;
+            u0 = a.U + ((int64_t)s0 * H + h) * DK * dv;
+            m_step = (int64_t)H * DK * DK;
+            u_step = (int64_t)H * DK * dv;
+            ldm = DK;
+            ldu = dv;
+            if (a.mode == WALK_COMPOSE) {
+                ucol = max(col - DK, 0);  // in bounds even where no U is read
+                has_u = col >= DK;        // uniform over the workgroup: 16 | DK
+            }
+        }
         f32x4 x[TT];
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) x[tt][s] = S_init[((int64_t)h * DK + row(tt, s)) * dv + col];
+            for (int s = 0; s < 4; ++s) {
+                const int rr = row(tt, s);
+                if (a.mode == WALK_COMPOSE)
+                    x[tt][s] = rr == col ? 1.f : 0.f;
+                else if (a.mode == WALK_SEGMENTS && s0 > 0)
+                    x[tt][s] = a.incoming[(((int64_t)s0 * H + h) * DK + rr) * dv + col];
+                else
+                    x[tt][s] = a.S_init[((int64_t)h * DK + rr) * dv + col];
+            }
         f32x4 ma[TT][KQ / 4], ua[TT];
         auto load = [&](int i) {
-            const int64_t kh = (int64_t)i * H + h;
+            const float *mb = m0 + i * m_step, *ub = u0 + i * u_step;
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
-                const float *Mr = M + (kh * DK + RW * w + 16 * tt + li) * DK + KQ * g;
+                const float *Mr = mb + (int64_t)(RW * w + 16 * tt + li) * ldm + KQ * g;
 #pragma unroll
                 for (int q = 0; q < KQ / 4; ++q) ma[tt][q] = *(const f32x4 *)(Mr + 4 * q);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) ua[tt][s] = U[(kh * DK + row(tt, s)) * dv + col];
+                for (int s = 0; s < 4; ++s) ua[tt][s] = has_u ? ub[(int64_t)row(tt, s) * ldu + ucol] : 0.f;
             }
         };
         load(0);
-        for (int i = 0; i < n_seg; ++i) {
-            const int64_t kh = (int64_t)i * H + h;
+        for (int i = 0; i < n_steps; ++i) {
+            if (a.mode == WALK_SEGMENTS) {
+                const int64_t kh = (int64_t)(s0 + i) * H + h;
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
+                for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) incoming[(kh * DK + row(tt, s)) * dv + col] = x[tt][s];
+                    for (int s = 0; s < 4; ++s) a.incoming[(kh * DK + row(tt, s)) * dv + col] = x[tt][s];
+            }
             __syncthreads();  // every wave is done reading the previous W from LDS
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
@@ -144,7 +197,7 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(int n_seg, int H
 #pragma unroll
                 for (int q = 0; q < KQ / 4; ++q) mc[tt][q] = ma[tt][q];
             }
-            if (i + 1 < n_seg) load(i + 1);  // in flight during this step
+            if (i + 1 < n_steps) load(i + 1);  // in flight during this step
 #pragma unroll
             for (int q = 0; q < KQ / 4; ++q)
 #pragma unroll
@@ -154,38 +207,100 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(int n_seg, int H
                     for (int tt = 0; tt < TT; ++tt) acc[tt] = mfma_f32x4(mc[tt][q][e], bx, acc[tt]);
                 }
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                x[tt] = acc[tt];
+            for (int tt = 0; tt < TT; ++tt) x[tt] = acc[tt];
+            if (a.mode == WALK_SEGMENTS) {
+                const int64_t kh = (int64_t)(s0 + i) * H + h;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) outgoing[(kh * DK + row(tt, s)) * dv + col] = x[tt][s];
+                for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) a.outgoing[(kh * DK + row(tt, s)) * dv + col] = x[tt][s];
+            } else if (a.mode == WALK_BLOCKS) {
+                // incoming state of block i + 1
+                const int64_t kh = (int64_t)((i + 1) * a.blk) * H + h;
+#pragma unroll
+                for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) a.incoming[(kh * DK + row(tt, s)) * dv + col] = x[tt][s];
             }
         }
+        if (a.mode == WALK_COMPOSE) {
+            float *cp = a.comp + ((int64_t)task * H + h) * DK * (DK + dv);
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+            for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) final_state[((int64_t)h * DK + row(tt, s)) * dv + col] = x[tt][s];
+                for (int s = 0; s < 4; ++s) cp[(int64_t)row(tt, s) * (DK + dv) + col] = x[tt][s];
+        } else if (a.mode == WALK_SEGMENTS && s0 + n_steps == a.n_seg) {
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) a.final_state[((int64_t)h * DK + row(tt, s)) * dv + col] = x[tt][s];
+        }
         __syncthreads();  // the next task's first W store waits for this one's readers
     }
+}
+
+template <int DK>
+static hipError_t launch_walk(const ScanWalk &a, hipStream_t stream) {
+    const int n_lin = 8 * a.n_task * ((a.H + 7) / 8) * (a.width / 16);
+    hipLaunchKernelGGL(kda_affine_scan_mfma<DK>, dim3(n_lin), dim3(SCAN_NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+static hipError_t launch_walk_dk(int dk, const ScanWalk &a, hipStream_t stream) {
+    return dk == 128 ? launch_walk<128>(a, stream) : launch_walk<64>(a, stream);
 }
 
 hipError_t launch_affine_scan(int n_seg, int H, int dk, int dv, const float *M, const float *U,
                               const float *S_init, float *incoming, float *outgoing, float *final_state,
                               hipStream_t stream) {
     if (dk == 128 || dk == 64) {
-        const int ncb = dv / 16;
-        const dim3 grid((H * ncb + 8 * ncb - 1) / (8 * ncb) * (8 * ncb));
-        if (dk == 128)
-            hipLaunchKernelGGL(kda_affine_scan_mfma<128>, grid, dim3(SCAN_NT), 0, stream, n_seg, H, dv, M, U,
-                               S_init, incoming, outgoing, final_state);
-        else
-            hipLaunchKernelGGL(kda_affine_scan_mfma<64>, grid, dim3(SCAN_NT), 0, stream, n_seg, H, dv, M, U,
-                               S_init, incoming, outgoing, final_state);
-        return hipGetLastError();
+        const ScanWalk a{WALK_SEGMENTS, n_seg, H, dv, n_seg, 1, dv, M, U, S_init, incoming, outgoing,
+                         final_state, nullptr};
+        return launch_walk_dk(dk, a, stream);
     }
     const dim3 grid(H * (dv / 16));
     hipLaunchKernelGGL(kda_affine_scan_kernel, grid, dim3(SCAN_NT), 0, stream, n_seg, H, dk, dv, M, U,
                        S_init, incoming, outgoing, final_state);
     return hipGetLastError();
+}
+
+int scan_block_size(int n_seg, int dk, int dv, int blk) {
+    if (blk <= 0) {
+        // three launches and about three times the work: below 32 segments the ordered
+        // walk is faster (16 segments x 8 heads at dk = dv = 128: 0.068 against 0.080 ms);
+        // above, a critical path of ~2 blk + n_seg / blk steps wants blk ~ sqrt(n_seg / 2)
+        if (n_seg < 32) return n_seg;
+        blk = 1;
+        while (2 * blk * blk < n_seg) ++blk;
+    }
+    // the block composites [dk, dk + dv] per block and head are kept in the outgoing
+    // stack (n_seg [dk, dv] per head) until the last launch overwrites it
+    const int min_blk = 1 + (dk + dv - 1) / dv;
+    blk = max(blk, min_blk);
+    return blk >= n_seg ? n_seg : blk;
+}
+
+hipError_t launch_affine_scan_blocked(int n_seg, int H, int dk, int dv, int blk, const float *M,
+                                      const float *U, const float *S_init, float *incoming,
+                                      float *outgoing, float *final_state, hipStream_t stream) {
+    if (!(dk == 128 || dk == 64))
+        return launch_affine_scan(n_seg, H, dk, dv, M, U, S_init, incoming, outgoing, final_state, stream);
+    blk = scan_block_size(n_seg, dk, dv, blk);
+    const int n_blocks = (n_seg + blk - 1) / blk;
+    hipError_t e = hipSuccess;
+    if (n_blocks > 1) {
+        const ScanWalk c{WALK_COMPOSE, n_seg, H, dv, blk, n_blocks - 1, dk + dv, M, U, S_init, incoming,
+                         outgoing, final_state, outgoing};
+        e = launch_walk_dk(dk, c, stream);
+        if (e != hipSuccess) return e;
+        const ScanWalk b{WALK_BLOCKS, n_seg, H, dv, blk, 1, dv, M, U, S_init, incoming, outgoing,
+                         final_state, outgoing};
+        e = launch_walk_dk(dk, b, stream);
+        if (e != hipSuccess) return e;
+    }
+    const ScanWalk s{WALK_SEGMENTS, n_seg, H, dv, blk, n_blocks, dv, M, U, S_init, incoming, outgoing,
+                     final_state, nullptr};
+    return launch_walk_dk(dk, s, stream);
 }
 
 }  // namespace kda

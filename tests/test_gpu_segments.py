@@ -192,3 +192,56 @@ def test_scan_random_maps(dk, dv, n, H):
         assert rel_fro(wl.as_f64(inc[:, h]), r["incoming_states"]) <= 1e-5
         assert rel_fro(wl.as_f64(outg[:, h]), r["outgoing_states"]) <= 1e-5
         assert rel_fro(wl.as_f64(fin[h]), r["final_state"]) <= 1e-5
+
+
+# ---- the blocked (regrouped) scan: KDA Context Parallelism, "Theory" (the composition
+# of segment maps is associative, so the ordered prefix may be regrouped, never reordered)
+
+def test_blocked_scan_scalar_example_exact():
+    with open(os.path.join(GOLDEN, "scalar_three_segment.json")) as f:
+        g = json.load(f)
+    d = 64  # the MFMA walk (dk 16 and 32 run the ordered scan)
+    eye = torch.eye(d, device="cuda")
+    ones = torch.ones(d, d, device="cuda")
+    M = torch.stack([m * eye for m in g["M"]]).unsqueeze(1)
+    U = torch.stack([u * ones for u in g["U"]]).unsqueeze(1)
+    S = (g["S_init"] * ones).unsqueeze(0)
+    assert kda.affine_scan_block_size(3, d, d, 2) == 2  # blocks {F0, F1}, {F2}
+    inc, outg, fin = kda.affine_exclusive_scan(M, U, S, block=2)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.all(inc[i] == g["incoming_states"][i])
+        assert torch.all(outg[i] == g["outgoing_states"][i])
+    assert torch.all(fin == g["final_state"])
+
+
+@pytest.mark.parametrize("dk,dv,n,H,block", [(128, 128, 48, 4, 0), (128, 128, 16, 8, 2), (128, 128, 17, 3, 5),
+                                             (128, 64, 10, 2, 0), (64, 128, 7, 2, 3), (64, 64, 9, 3, 4),
+                                             (64, 64, 40, 2, 0), (128, 128, 1, 2, 0), (128, 128, 6, 2, 6)])
+def test_blocked_scan_random_maps(dk, dv, n, H, block):
+    from oracle import oracle as orc
+    from kda_testlib import rel_fro
+    g = torch.Generator(device="cpu").manual_seed(7 * dk + n + block)
+    M = (torch.eye(dk) + 0.1 * torch.randn(n, H, dk, dk, generator=g) / dk ** 0.5).float()
+    U = torch.randn(n, H, dk, dv, generator=g).float()
+    S = torch.randn(H, dk, dv, generator=g).float()
+    Md, Ud, Sd = M.cuda(), U.cuda(), S.cuda()
+    blk = kda.affine_scan_block_size(n, dk, dv, block)
+    inc, outg, fin = kda.affine_exclusive_scan(Md, Ud, Sd, block=block)
+    inc0, outg0, fin0 = kda.affine_exclusive_scan(Md, Ud, Sd)
+    torch.cuda.synchronize()
+    assert torch.equal(Md.cpu(), M) and torch.equal(Ud.cpu(), U) and torch.equal(Sd.cpu(), S)
+    worst = 0.0
+    for h in range(H):
+        r = orc.scan(M[:, h].double().numpy(), U[:, h].double().numpy(), S[h].double().numpy())
+        for got, key in ((inc[:, h], "incoming_states"), (outg[:, h], "outgoing_states"), (fin[h], "final_state")):
+            e = rel_fro(wl.as_f64(got), r[key])
+            worst = max(worst, e)
+            assert e <= 1e-5, (h, key, e)
+    # the regrouped products differ from the ordered walk by fp32 rounding only
+    for a, b in ((inc, inc0), (outg, outg0), (fin, fin0)):
+        assert rel_fro(wl.as_f64(a), wl.as_f64(b)) <= 1e-5
+    if blk >= n:
+        # one block is the ordered walk itself
+        assert torch.equal(inc, inc0) and torch.equal(outg, outg0) and torch.equal(fin, fin0)
+    print(f"blocked scan dk={dk} dv={dv} n_seg={n} H={H}: blocks of {blk}, worst rel err vs oracle {worst:.2e}")

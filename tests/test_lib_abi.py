@@ -208,6 +208,32 @@ def test_summary_and_scan_error_paths(L):
     assert L.kda_affine_exclusive_scan(2, 2, 48, 16, *sargs, None) == EUNSUP
     assert L.kda_affine_exclusive_scan(2, 2, 16, 8, *sargs, None) == EUNSUP
     assert L.kda_affine_exclusive_scan(2, 2, 16, 16, None, *sargs[1:], None) == ENULL
+    blk = L.kda_affine_exclusive_scan_blocked
+    assert blk(0, 2, 64, 64, 0, *sargs, None) == ESHAPE                                 # n_seg >= 1
+    assert blk(4, 2, 64, 64, -1, *sargs, None) == ESHAPE                                # block >= 0
+    assert blk(4, 2, 48, 64, 0, *sargs, None) == EUNSUP
+    assert blk(4, 2, 64, 8, 0, *sargs, None) == EUNSUP
+    assert blk(4, 2, 64, 64, 0, *sargs[:5], None, None) == ENULL
+
+
+def test_scan_block_size_rule(L):
+    """Automatic: the ordered scan below 32 segments, else blocks of about sqrt(n_seg / 2)
+    segments (critical path ~ 2 block + n_seg / block map steps).  Any block is raised to
+    at least 1 + ceil(dk / dv) so that the block composites fit in the outgoing stack, and
+    is n_seg (the ordered scan) when one block holds everything or dk is 16 or 32."""
+    bs = L.kda_affine_scan_block_size
+    assert [bs(n, 128, 128, 0) for n in (1, 2, 3, 16, 31, 32, 64, 200)] == [1, 2, 3, 16, 31, 4, 6, 10]
+    assert bs(16, 128, 128, 5) == 5 and bs(16, 128, 128, 1) == 2   # raised to 1 + dk/dv
+    assert bs(16, 128, 64, 1) == 3 and bs(16, 64, 128, 1) == 2
+    assert bs(16, 128, 128, 16) == 16 and bs(16, 128, 128, 40) == 16
+    assert bs(16, 32, 32, 4) == 16                                  # ordered walk at dk 32
+    assert bs(0, 128, 128, 0) == -1 and bs(4, 128, 128, -2) == -1
+    # the composites of all blocks but the last fit in the outgoing stack
+    for n in range(1, 80):
+        for dk, dv in ((128, 128), (128, 64), (64, 128), (64, 64)):
+            b = bs(n, dk, dv, 0)
+            nb = -(-n // b)
+            assert (nb - 1) * dk * (dk + dv) <= n * dk * dv
     assert L.kda_validate_varlen(FAKE, -1, 0, FAKE, 4) == ESHAPE
     assert L.kda_validate_varlen(None, 2, 0, FAKE, 4) == ENULL
 
