@@ -463,17 +463,25 @@ __global__ __launch_bounds__(256) void piece_scan_kernel(PieceArgs p) {
 // and head), decodes them from the piece table staged once in LDS, and stages X_k^T (bf16,
 // written by piece_scan_kernel) in LDS when the piece or head changes.  Wave w owns the
 // 16 tokens 16w .. 16w+15 of the chunk and all dv columns, C^T = X^T W^T with 16x16x32
-// bf16 MFMAs: each W row is read once, and a lane adds 4 consecutive columns of one token
-// per column tile (8-byte read-modify-writes).
+// bf16 MFMAs: each W row is read once.  The column tiles go in pairs whose A rows are
+// permuted (fix_col) so that a lane's outputs of the pair are 8 consecutive columns of one
+// token: 16-byte read-modify-writes of out, 64 contiguous bytes per token and instruction.
 constexpr int FIX_NP = 256;   // pieces staged in LDS (more: read from global memory)
 constexpr int FIX_TASKS = 4;  // tasks per group (1, 2 and 4 measured within 10% of each other)
+
+// Column of out (row of X^T) behind A row li of column tile 2q + hf: the lane quarter g of
+// the pair's outputs then holds columns 32q + 8g .. 32q + 8g + 7.
+__device__ __forceinline__ int fix_col(int q, int hf, int li) { return 32 * q + 8 * (li >> 2) + 4 * hf + (li & 3); }
+// Staged X^T row r: a pitch of dk + 8 elements plus 32 elements (four groups of 4 LDS banks)
+// per 16 rows, so that the 16 rows of a permuted tile start in distinct bank groups.
+template <int DK>
+__device__ __forceinline__ int fix_row(int r) { return r * (DK + 8) + 32 * (r >> 4); }
 
 template <int DK>
 __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
     constexpr int DV = DK;
-    constexpr int FIX_XP = DK + 8;  // bf16 pitch of the staged X^T rows
     __shared__ int4 spc[FIX_NP];
-    __shared__ __attribute__((aligned(16))) bf16_t sxt[DV * FIX_XP];
+    __shared__ __attribute__((aligned(16))) bf16_t sxt[DV * (DK + 8) + 32 * (DV / 16)];
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
     const int H = p.H;
     const int n_piece = p.hdr->n_piece;
@@ -518,12 +526,12 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         return k;
     };
     bf16x8 bw[DK / 32];
-    bf16x4 ov[DV / 16];
-    auto load = [&](const Task &k, bf16x8 (&b)[DK / 32], bf16x4 (&o)[DV / 16]) {
+    bf16x8 ov[DV / 32];
+    auto load = [&](const Task &k, bf16x8 (&b)[DK / 32], bf16x8 (&o)[DV / 32]) {
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) b[kb] = *(const bf16x8 *)(p.W + k.roww * DK + 32 * kb + 8 * g);
 #pragma unroll
-        for (int ct = 0; ct < DV / 16; ++ct) o[ct] = *(const bf16x4 *)(p.out + k.rowh * DV + 16 * ct + 4 * g);
+        for (int q = 0; q < DV / 32; ++q) o[q] = *(const bf16x8 *)(p.out + k.rowh * DV + 32 * q + 8 * g);
     };
     int cur = -1;
     int64_t tk = task_of(0);  // valid: this workgroup has at least one task
@@ -535,7 +543,7 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
         const int64_t tn = task_of(k + 1);
         Task nt = tc;
         bf16x8 bwn[DK / 32];
-        bf16x4 ovn[DV / 16];
+        bf16x8 ovn[DV / 32];
         if (tn >= 0) {  // uniform over the workgroup
             nt = decode(tn);
             load(nt, bwn, ovn);
@@ -546,28 +554,31 @@ __global__ __launch_bounds__(256) void fixup_kernel(PieceArgs p) {
 #pragma unroll
             for (int i = 0; i < DV * DK / (8 * 256); ++i) {
                 const int e = 8 * (t + 256 * i), r = e / DK, cc = e - r * DK;
-                *(bf16x8 *)(sxt + r * FIX_XP + cc) = *(const bf16x8 *)(xt + e);
+                *(bf16x8 *)(sxt + fix_row<DK>(r) + cc) = *(const bf16x8 *)(xt + e);
             }
             __syncthreads();
             cur = tc.key;
         }
         // a wave past the end of a short chunk only joins the barriers
         const bool store = 16 * w + li < tc.n;
-        bf16_t *o = p.out + ((int64_t)(tc.t0 + 16 * w + li) * H + tc.h) * DV + 4 * g;
+        bf16_t *o = p.out + ((int64_t)(tc.t0 + 16 * w + li) * H + tc.h) * DV + 8 * g;
 #pragma unroll
-        for (int ct = 0; ct < DV / 16; ++ct) {
-            f32x4 acc = f4(ov[ct]);
+        for (int q = 0; q < DV / 32; ++q) {
+            const bf16x8 oq = ov[q];
+            f32x4 acc0 = f4(bf16x4{oq[0], oq[1], oq[2], oq[3]}), acc1 = f4(bf16x4{oq[4], oq[5], oq[6], oq[7]});
 #pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb)
-                acc = mfma(*(const bf16x8 *)(sxt + (16 * ct + li) * FIX_XP + 32 * kb + 8 * g), bw[kb], acc);
-            if (store) *(bf16x4 *)(o + 16 * ct) = bf4(acc);
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                acc0 = mfma(*(const bf16x8 *)(sxt + fix_row<DK>(fix_col(q, 0, li)) + 32 * kb + 8 * g), bw[kb], acc0);
+                acc1 = mfma(*(const bf16x8 *)(sxt + fix_row<DK>(fix_col(q, 1, li)) + 32 * kb + 8 * g), bw[kb], acc1);
+            }
+            if (store) *(bf16x8 *)(o + 32 * q) = cat(bf4(acc0), bf4(acc1));
         }
         tk = tn;
         tc = nt;
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) bw[kb] = bwn[kb];
 #pragma unroll
-        for (int ct = 0; ct < DV / 16; ++ct) ov[ct] = ovn[ct];
+        for (int q = 0; q < DV / 32; ++q) ov[q] = ovn[q];
     }
 }
 
