@@ -219,6 +219,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter scale)")
+    ap.add_argument("--scan-variants", action="store_true",
+                    help="segments workloads: also time the exclusive scan alone, ordered against "
+                         "blocked, at 16, 64 and 256 segments")
     ap.add_argument("--mfma-calibration", action="store_true",
                     help="also run a kernel of known MFMA count (MFMA-busy counter scale)")
     args = ap.parse_args()
@@ -524,7 +527,7 @@ def run_segments(args, w):
                          w, "kda_fast_kernel" if w.dtype == "bf16" and w.gate_mode == 1 and w.lower_bound >= -5.3
                          else "kda_chain_kernel")},
         "per_call": protocol,
-        "scan_variants": scan_variants(dev, w.H, w.dk, w.dv) if w.dk in (64, 128) else None,
+        "scan_variants": scan_variants(dev, w.H, w.dk, w.dv) if args.scan_variants and w.dk in (64, 128) else None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
