@@ -109,7 +109,7 @@ struct ScanWalk {
     float *comp;  // block composites (WALK_COMPOSE writes, WALK_BLOCKS reads)
 };
 
-template <int DK>
+template <int DK, int MODE>
 __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
     constexpr int TT = DK / 64, RW = DK / 4, KQ = DK / 4;
     __shared__ float sx[16 * DK + 16 * 4];
@@ -125,64 +125,69 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
         if (h >= H) continue;  // uniform over the workgroup
         const int col = 16 * cb + li;
         auto row = [&](int tt, int s) { return RW * w + 16 * tt + 4 * g + s; };
-        // the task's maps: step i reads M rows at m0 + i m_step (row pitch ldm) and U
-        // column ucol at u0 + i u_step (row pitch ldu); no U for the identity columns
-        const int s0 = a.mode == WALK_BLOCKS ? 0 : task * a.blk;
-        const int n_steps = a.mode == WALK_BLOCKS ? (a.n_seg + a.blk - 1) / a.blk - 1 : min(a.blk, a.n_seg - s0);
+        // Addresses are a wave-uniform base per step (scalar) plus 32-bit lane offsets:
+        // step i reads the M rows of its map at mb(i) (row pitch ldm) and U column ucol at
+        // ub(i) (row pitch ldu), and writes state rows at sb(i) (row pitch dv).
+        const int s0 = MODE == WALK_BLOCKS ? 0 : task * a.blk;
+        const int n_steps = MODE == WALK_BLOCKS ? (a.n_seg + a.blk - 1) / a.blk - 1 : min(a.blk, a.n_seg - s0);
+        const int ldm = MODE == WALK_BLOCKS ? DK + dv : DK, ldu = MODE == WALK_BLOCKS ? DK + dv : dv;
+        const int64_t hs = (int64_t)H * DK;  // one step of a [*, H, DK, ...] stack, in rows
         const float *m0, *u0;
         int64_t m_step, u_step;
-        int ldm, ldu, ucol = col;
+        int ucol = col;
         bool has_u = true;
-        if (a.mode == WALK_BLOCKS) {
+        if constexpr (MODE == WALK_BLOCKS) {
             m0 = a.comp + (int64_t)h * DK * (DK + dv);
             u0 = m0 + DK;
-            m_step = u_step = (int64_t)H * DK * (DK + dv);
-            ldm = ldu = DK + dv;
+            m_step = u_step = hs * (DK + dv);
         } else {
             m0 = a.M + ((int64_t)s0 * H + h) * DK * DK;
             u0 = a.U + ((int64_t)s0 * H + h) * DK * dv;
-            m_step = (int64_t)H * DK * DK;
-            u_step = (int64_t)H * DK * dv;
-            ldm = DK;
-            ldu = dv;
-            if (a.mode == WALK_COMPOSE) {
+            m_step = hs * DK;
+            u_step = hs * dv;
+            if constexpr (MODE == WALK_COMPOSE) {
                 ucol = max(col - DK, 0);  // in bounds even where no U is read
                 has_u = col >= DK;        // uniform over the workgroup: 16 | DK
             }
         }
+        const int mo = (RW * w + li) * ldm + KQ * g;      // + 16 tt ldm + 4 q
+        const int uo = (RW * w + 4 * g) * ldu + ucol;     // + (16 tt + s) ldu
+        const int so = (RW * w + 4 * g) * dv + col;       // + (16 tt + s) dv
+        float *const inc0 = a.incoming + ((int64_t)s0 * H + h) * DK * dv;
+        float *const out0 = a.outgoing + ((int64_t)s0 * H + h) * DK * dv;
+        const int64_t s_step = hs * dv;
         f32x4 x[TT];
+        {
+            const float *src = MODE == WALK_SEGMENTS && s0 > 0 ? inc0 : a.S_init + (int64_t)h * DK * dv;
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+            for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int rr = row(tt, s);
-                if (a.mode == WALK_COMPOSE)
-                    x[tt][s] = rr == col ? 1.f : 0.f;
-                else if (a.mode == WALK_SEGMENTS && s0 > 0)
-                    x[tt][s] = a.incoming[(((int64_t)s0 * H + h) * DK + rr) * dv + col];
-                else
-                    x[tt][s] = a.S_init[((int64_t)h * DK + rr) * dv + col];
-            }
+                for (int s = 0; s < 4; ++s) {
+                    if constexpr (MODE == WALK_COMPOSE)
+                        x[tt][s] = row(tt, s) == col ? 1.f : 0.f;
+                    else
+                        x[tt][s] = src[so + (16 * tt + s) * dv];
+                }
+        }
         f32x4 ma[TT][KQ / 4], ua[TT];
         auto load = [&](int i) {
             const float *mb = m0 + i * m_step, *ub = u0 + i * u_step;
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
-                const float *Mr = mb + (int64_t)(RW * w + 16 * tt + li) * ldm + KQ * g;
 #pragma unroll
-                for (int q = 0; q < KQ / 4; ++q) ma[tt][q] = *(const f32x4 *)(Mr + 4 * q);
+                for (int q = 0; q < KQ / 4; ++q) ma[tt][q] = *(const f32x4 *)(mb + mo + 16 * tt * ldm + 4 * q);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) ua[tt][s] = has_u ? ub[(int64_t)row(tt, s) * ldu + ucol] : 0.f;
+                for (int s = 0; s < 4; ++s) ua[tt][s] = has_u ? ub[uo + (16 * tt + s) * ldu] : 0.f;
             }
         };
         load(0);
         for (int i = 0; i < n_steps; ++i) {
-            if (a.mode == WALK_SEGMENTS) {
-                const int64_t kh = (int64_t)(s0 + i) * H + h;
+            if constexpr (MODE == WALK_SEGMENTS) {
+                float *ib = inc0 + i * s_step;
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) a.incoming[(kh * DK + row(tt, s)) * dv + col] = x[tt][s];
+                    for (int s = 0; s < 4; ++s) ib[so + (16 * tt + s) * dv] = x[tt][s];
             }
             __syncthreads();  // every wave is done reading the previous W from LDS
 #pragma unroll
@@ -208,28 +213,28 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
                 }
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) x[tt] = acc[tt];
-            if (a.mode == WALK_SEGMENTS) {
-                const int64_t kh = (int64_t)(s0 + i) * H + h;
+            if constexpr (MODE == WALK_SEGMENTS) {
+                float *ob = out0 + i * s_step;
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) a.outgoing[(kh * DK + row(tt, s)) * dv + col] = x[tt][s];
-            } else if (a.mode == WALK_BLOCKS) {
+                    for (int s = 0; s < 4; ++s) ob[so + (16 * tt + s) * dv] = x[tt][s];
+            } else if constexpr (MODE == WALK_BLOCKS) {
                 // incoming state of block i + 1
-                const int64_t kh = (int64_t)((i + 1) * a.blk) * H + h;
+                float *ib = a.incoming + ((int64_t)((i + 1) * a.blk) * H + h) * DK * dv;
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) a.incoming[(kh * DK + row(tt, s)) * dv + col] = x[tt][s];
+                    for (int s = 0; s < 4; ++s) ib[so + (16 * tt + s) * dv] = x[tt][s];
             }
         }
-        if (a.mode == WALK_COMPOSE) {
+        if constexpr (MODE == WALK_COMPOSE) {
             float *cp = a.comp + ((int64_t)task * H + h) * DK * (DK + dv);
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) cp[(int64_t)row(tt, s) * (DK + dv) + col] = x[tt][s];
-        } else if (a.mode == WALK_SEGMENTS && s0 + n_steps == a.n_seg) {
+        } else if (MODE == WALK_SEGMENTS && s0 + n_steps == a.n_seg) {
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
@@ -241,8 +246,13 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
 
 template <int DK>
 static hipError_t launch_walk(const ScanWalk &a, hipStream_t stream) {
-    const int n_lin = 8 * a.n_task * ((a.H + 7) / 8) * (a.width / 16);
-    hipLaunchKernelGGL(kda_affine_scan_mfma<DK>, dim3(n_lin), dim3(SCAN_NT), 0, stream, a);
+    const dim3 grid(8 * a.n_task * ((a.H + 7) / 8) * (a.width / 16));
+    if (a.mode == WALK_COMPOSE)
+        hipLaunchKernelGGL((kda_affine_scan_mfma<DK, WALK_COMPOSE>), grid, dim3(SCAN_NT), 0, stream, a);
+    else if (a.mode == WALK_BLOCKS)
+        hipLaunchKernelGGL((kda_affine_scan_mfma<DK, WALK_BLOCKS>), grid, dim3(SCAN_NT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((kda_affine_scan_mfma<DK, WALK_SEGMENTS>), grid, dim3(SCAN_NT), 0, stream, a);
     return hipGetLastError();
 }
 
