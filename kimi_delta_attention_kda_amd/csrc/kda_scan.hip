@@ -277,7 +277,7 @@ hipError_t launch_affine_scan(int n_seg, int H, int dk, int dv, const float *M, 
 int scan_block_size(int n_seg, int dk, int dv, int blk) {
     if (blk <= 0) {
         // three launches and about three times the work: below 32 segments the ordered
-        // walk is faster (16 segments x 8 heads at dk = dv = 128: 0.068 against 0.080 ms);
+        // walk is faster (16 segments x 8 heads at dk = dv = 128: 0.056 against 0.080 ms);
         // above, a critical path of ~2 blk + n_seg / blk steps wants blk ~ sqrt(n_seg / 2)
         if (n_seg < 32) return n_seg;
         blk = 1;
