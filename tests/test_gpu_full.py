@@ -2,7 +2,8 @@
 
 The oracle recomputes (sequence, head) pairs token by token on every host core, and each
 pair is compared whole (every output row and the final state): all 256 pairs of the
-32K-token batch (at dk = 128 and 64), all 32 heads of the 131K-token sequence, and 2,048
+32K-token batch (at dk = 128 and 64, and with the original gate), all 32 heads of the
+131K-token sequence, and 2,048
 of the 16,384 pairs of the 512-sequence batch (every sequence, four heads each).
 Properties that hold at any size (untouched pool slots bit-identical, run-to-run
 determinism, continuation across calls) are checked on the whole tensors.
@@ -36,7 +37,7 @@ def _check(w, inp, out, pool, items):
     assert es <= STATE_TOL
 
 
-@pytest.mark.parametrize("name", ["varlen_32k", "varlen_32k_dk64"])
+@pytest.mark.parametrize("name", ["varlen_32k", "varlen_32k_dk64", "varlen_32k_original"])
 def test_varlen_32k(name):
     from kda_testlib import run_fwd, untouched_slots_identical
     w = wl.workload(name)
