@@ -10,6 +10,8 @@
 //    (the next segment's M and U are loaded while the current step computes), W sits in
 //    LDS, and the column blocks of one head run on one XCD so M_i comes from HBM once.
 //  - dk in {16, 32}: fp32 FMA with M_i staged in LDS.
+#include <algorithm>
+
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -116,11 +118,13 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
     const int H = a.H, dv = a.dv;
     const int ncb = a.width / 16, n_hh = (H + 7) / 8;
-    const int n_lin = 8 * a.n_task * n_hh * ncb;
-    for (int lin = blockIdx.x; lin < n_lin; lin += gridDim.x) {
+    const int64_t n_lin = 8 * (int64_t)a.n_task * n_hh * ncb;
+    for (int64_t lin = blockIdx.x; lin < n_lin; lin += gridDim.x) {
         // workgroups are dealt to the 8 XCDs round-robin: lin & 7 picks the XCD, and every
         // column block of a head runs on the same one, so each map comes from HBM once
-        const int r = lin >> 3, cb = r % ncb, hh = (r / ncb) % n_hh, task = r / (ncb * n_hh);
+        // (a grid stride that is a multiple of 8 keeps each workgroup on its XCD)
+        const int64_t r = lin >> 3;
+        const int cb = (int)(r % ncb), hh = (int)((r / ncb) % n_hh), task = (int)(r / (ncb * n_hh));
         const int h = 8 * hh + (lin & 7);
         if (h >= H) continue;  // uniform over the workgroup
         const int col = 16 * cb + li;
@@ -246,7 +250,9 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
 
 template <int DK>
 static hipError_t launch_walk(const ScanWalk &a, hipStream_t stream) {
-    const dim3 grid(8 * a.n_task * ((a.H + 7) / 8) * (a.width / 16));
+    // one workgroup per (task, head, 16 columns), at most 2^20 at once (the kernel strides)
+    const int64_t n_lin = 8 * (int64_t)a.n_task * ((a.H + 7) / 8) * (a.width / 16);
+    const dim3 grid((unsigned)std::min<int64_t>(n_lin, (int64_t)1 << 20));
     if (a.mode == WALK_COMPOSE)
         hipLaunchKernelGGL((kda_affine_scan_mfma<DK, WALK_COMPOSE>), grid, dim3(SCAN_NT), 0, stream, a);
     else if (a.mode == WALK_BLOCKS)

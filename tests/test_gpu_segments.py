@@ -245,3 +245,26 @@ def test_blocked_scan_random_maps(dk, dv, n, H, block):
         # one block is the ordered walk itself
         assert torch.equal(inc, inc0) and torch.equal(outg, outg0) and torch.equal(fin, fin0)
     print(f"blocked scan dk={dk} dv={dv} n_seg={n} H={H}: blocks of {blk}, worst rel err vs oracle {worst:.2e}")
+
+
+def test_blocked_scan_grid_stride():
+    """53,000 segments in blocks of 2 at dk = 64, dv = 16: the compose launch has more
+    workgroups' worth of tasks than the 2^20 it launches, so workgroups take a second task
+    by grid stride.  Contractive maps (M = 0.99 I + noise) keep the state bounded."""
+    from oracle import oracle as orc
+    from kda_testlib import rel_fro
+    n, H, dk, dv = 53000, 1, 64, 16
+    g = torch.Generator(device="cuda").manual_seed(5)
+    M = 0.99 * torch.eye(dk, device="cuda") + 0.01 * torch.randn(n, H, dk, dk, generator=g, device="cuda") / dk ** 0.5
+    U = torch.randn(n, H, dk, dv, generator=g, device="cuda")
+    S = torch.randn(H, dk, dv, generator=g, device="cuda")
+    assert 8 * (-(-n // 2) - 1) * ((dk + dv) // 16) > 1 << 20
+    inc, outg, fin = kda.affine_exclusive_scan(M, U, S, block=2)
+    inc0, outg0, fin0 = kda.affine_exclusive_scan(M, U, S)
+    torch.cuda.synchronize()
+    for a, b in ((inc, inc0), (outg, outg0), (fin, fin0)):
+        assert rel_fro(wl.as_f64(a), wl.as_f64(b)) <= 1e-5
+    r = orc.scan(M[:, 0].double().cpu().numpy(), U[:, 0].double().cpu().numpy(), S[0].double().cpu().numpy())
+    e = max(rel_fro(wl.as_f64(inc[:, 0]), r["incoming_states"]), rel_fro(wl.as_f64(fin[0]), r["final_state"]))
+    print(f"blocked scan, {n} segments in blocks of 2 (grid stride): rel err vs oracle {e:.2e}")
+    assert e <= 1e-5
