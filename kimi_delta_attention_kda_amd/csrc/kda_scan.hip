@@ -88,8 +88,12 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_kernel(int n_seg, int
 __device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// W in LDS column by column: column c of the workgroup's 16 CT at c (DK + 4), so that a
+// lane reads the four contraction entries of an MFMA group with one 16-byte read, and the
+// 16 lanes of a read phase (16 columns, pitch 132 floats) start in distinct groups of
+// four banks; a lane writes its four consecutive state rows with one 16-byte write.
 template <int DK>
-__device__ __forceinline__ int wx_at(int k, int c) { return 16 * k + c + 16 * (k / (DK / 4)); }
+__device__ __forceinline__ int wx_at(int k, int c) { return c * (DK + 4) + k; }
 
 // What one launch of the walk does.  The composition is associative (KDA Context
 // Parallelism, "Theory"), so the ordered prefix may be regrouped into blocks of blk
@@ -111,13 +115,17 @@ struct ScanWalk {
     float *comp;  // block composites (WALK_COMPOSE writes, WALK_BLOCKS reads)
 };
 
-template <int DK, int MODE>
+// A workgroup walks 16 CT state columns of one (task, head).  CT = 1 when few workgroups
+// run (the ordered walk is a chain of dependent steps: more, narrower workgroups shorten
+// each step); CT = 4 when the tasks fill the chip many times over, so that a map's rows,
+// loaded once per step, serve 64 columns (four times fewer reads of each map from L2).
+template <int DK, int MODE, int CT>
 __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
     constexpr int TT = DK / 64, RW = DK / 4, KQ = DK / 4;
-    __shared__ float sx[16 * DK + 16 * 4];
+    __shared__ __attribute__((aligned(16))) float sx[16 * CT * (DK + 4)];
     const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 4, li = l & 15;
     const int H = a.H, dv = a.dv;
-    const int ncb = a.width / 16, n_hh = (H + 7) / 8;
+    const int ncb = a.width / (16 * CT), n_hh = (H + 7) / 8;
     const int64_t n_lin = 8 * (int64_t)a.n_task * n_hh * ncb;
     for (int64_t lin = blockIdx.x; lin < n_lin; lin += gridDim.x) {
         // workgroups are dealt to the 8 XCDs round-robin: lin & 7 picks the XCD, and every
@@ -127,7 +135,7 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
         const int cb = (int)(r % ncb), hh = (int)((r / ncb) % n_hh), task = (int)(r / (ncb * n_hh));
         const int h = 8 * hh + (lin & 7);
         if (h >= H) continue;  // uniform over the workgroup
-        const int col = 16 * cb + li;
+        const int col = 16 * CT * cb + li;  // column of tile c: col + 16 c
         auto row = [&](int tt, int s) { return RW * w + 16 * tt + 4 * g + s; };
         // Addresses are a wave-uniform base per step (scalar) plus 32-bit lane offsets:
         // step i reads the M rows of its map at mb(i) (row pitch ldm) and U column ucol at
@@ -150,30 +158,33 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
             m_step = hs * DK;
             u_step = hs * dv;
             if constexpr (MODE == WALK_COMPOSE) {
+                // the workgroup's 16 CT columns are all M or all U columns: 16 CT divides DK
                 ucol = max(col - DK, 0);  // in bounds even where no U is read
-                has_u = col >= DK;        // uniform over the workgroup: 16 | DK
+                has_u = col >= DK;
             }
         }
         const int mo = (RW * w + li) * ldm + KQ * g;      // + 16 tt ldm + 4 q
-        const int uo = (RW * w + 4 * g) * ldu + ucol;     // + (16 tt + s) ldu
-        const int so = (RW * w + 4 * g) * dv + col;       // + (16 tt + s) dv
+        const int uo = (RW * w + 4 * g) * ldu + ucol;     // + (16 tt + s) ldu + 16 c
+        const int so = (RW * w + 4 * g) * dv + col;       // + (16 tt + s) dv + 16 c
         float *const inc0 = a.incoming + ((int64_t)s0 * H + h) * DK * dv;
         float *const out0 = a.outgoing + ((int64_t)s0 * H + h) * DK * dv;
         const int64_t s_step = hs * dv;
-        f32x4 x[TT];
+        f32x4 x[TT][CT];
         {
             const float *src = MODE == WALK_SEGMENTS && s0 > 0 ? inc0 : a.S_init + (int64_t)h * DK * dv;
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    if constexpr (MODE == WALK_COMPOSE)
-                        x[tt][s] = row(tt, s) == col ? 1.f : 0.f;
-                    else
-                        x[tt][s] = src[so + (16 * tt + s) * dv];
-                }
+                for (int c = 0; c < CT; ++c)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        if constexpr (MODE == WALK_COMPOSE)
+                            x[tt][c][s] = row(tt, s) == col + 16 * c ? 1.f : 0.f;
+                        else
+                            x[tt][c][s] = src[so + (16 * tt + s) * dv + 16 * c];
+                    }
         }
-        f32x4 ma[TT][KQ / 4], ua[TT];
+        f32x4 ma[TT][KQ / 4], ua[TT][CT];
         auto load = [&](int i) {
             const float *mb = m0 + i * m_step, *ub = u0 + i * u_step;
 #pragma unroll
@@ -181,7 +192,9 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
 #pragma unroll
                 for (int q = 0; q < KQ / 4; ++q) ma[tt][q] = *(const f32x4 *)(mb + mo + 16 * tt * ldm + 4 * q);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) ua[tt][s] = has_u ? ub[uo + (16 * tt + s) * ldu] : 0.f;
+                for (int c = 0; c < CT; ++c)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) ua[tt][c][s] = has_u ? ub[uo + (16 * tt + s) * ldu + 16 * c] : 0.f;
             }
         };
         load(0);
@@ -191,18 +204,21 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) ib[so + (16 * tt + s) * dv] = x[tt][s];
+                    for (int c = 0; c < CT; ++c)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) ib[so + (16 * tt + s) * dv + 16 * c] = x[tt][c][s];
             }
             __syncthreads();  // every wave is done reading the previous W from LDS
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) sx[wx_at<DK>(row(tt, s), li)] = x[tt][s];
+                for (int c = 0; c < CT; ++c) *(f32x4 *)(sx + wx_at<DK>(row(tt, 0), 16 * c + li)) = x[tt][c];
             __syncthreads();
-            f32x4 mc[TT][KQ / 4], acc[TT];
+            f32x4 mc[TT][KQ / 4], acc[TT][CT];
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
-                acc[tt] = ua[tt];
+#pragma unroll
+                for (int c = 0; c < CT; ++c) acc[tt][c] = ua[tt][c];
 #pragma unroll
                 for (int q = 0; q < KQ / 4; ++q) mc[tt][q] = ma[tt][q];
             }
@@ -210,26 +226,34 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
 #pragma unroll
             for (int q = 0; q < KQ / 4; ++q)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float bx = sx[wx_at<DK>(KQ * g + 4 * q + e, li)];
+                for (int c = 0; c < CT; ++c) {
+                    const f32x4 bx = *(const f32x4 *)(sx + wx_at<DK>(KQ * g + 4 * q, 16 * c + li));
 #pragma unroll
-                    for (int tt = 0; tt < TT; ++tt) acc[tt] = mfma_f32x4(mc[tt][q][e], bx, acc[tt]);
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int tt = 0; tt < TT; ++tt) acc[tt][c] = mfma_f32x4(mc[tt][q][e], bx[e], acc[tt][c]);
                 }
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) x[tt] = acc[tt];
+            for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+                for (int c = 0; c < CT; ++c) x[tt][c] = acc[tt][c];
             if constexpr (MODE == WALK_SEGMENTS) {
                 float *ob = out0 + i * s_step;
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) ob[so + (16 * tt + s) * dv] = x[tt][s];
+                    for (int c = 0; c < CT; ++c)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) ob[so + (16 * tt + s) * dv + 16 * c] = x[tt][c][s];
             } else if constexpr (MODE == WALK_BLOCKS) {
                 // incoming state of block i + 1
                 float *ib = a.incoming + ((int64_t)((i + 1) * a.blk) * H + h) * DK * dv;
 #pragma unroll
                 for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) ib[so + (16 * tt + s) * dv] = x[tt][s];
+                    for (int c = 0; c < CT; ++c)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) ib[so + (16 * tt + s) * dv + 16 * c] = x[tt][c][s];
             }
         }
         if constexpr (MODE == WALK_COMPOSE) {
@@ -237,29 +261,45 @@ __global__ __launch_bounds__(SCAN_NT) void kda_affine_scan_mfma(ScanWalk a) {
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) cp[(int64_t)row(tt, s) * (DK + dv) + col] = x[tt][s];
+                for (int c = 0; c < CT; ++c)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) cp[(int64_t)row(tt, s) * (DK + dv) + col + 16 * c] = x[tt][c][s];
         } else if (MODE == WALK_SEGMENTS && s0 + n_steps == a.n_seg) {
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) a.final_state[((int64_t)h * DK + row(tt, s)) * dv + col] = x[tt][s];
+                for (int c = 0; c < CT; ++c)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        a.final_state[((int64_t)h * DK + row(tt, s)) * dv + col + 16 * c] = x[tt][c][s];
         }
         __syncthreads();  // the next task's first W store waits for this one's readers
     }
 }
 
-template <int DK>
-static hipError_t launch_walk(const ScanWalk &a, hipStream_t stream) {
-    // one workgroup per (task, head, 16 columns), at most 2^20 at once (the kernel strides)
-    const int64_t n_lin = 8 * (int64_t)a.n_task * ((a.H + 7) / 8) * (a.width / 16);
+template <int DK, int CT>
+static hipError_t launch_walk_ct(const ScanWalk &a, hipStream_t stream) {
+    // one workgroup per (task, head, 16 CT columns), at most 2^20 at once (the kernel strides)
+    const int64_t n_lin = 8 * (int64_t)a.n_task * ((a.H + 7) / 8) * (a.width / (16 * CT));
     const dim3 grid((unsigned)std::min<int64_t>(n_lin, (int64_t)1 << 20));
     if (a.mode == WALK_COMPOSE)
-        hipLaunchKernelGGL((kda_affine_scan_mfma<DK, WALK_COMPOSE>), grid, dim3(SCAN_NT), 0, stream, a);
+        hipLaunchKernelGGL((kda_affine_scan_mfma<DK, WALK_COMPOSE, CT>), grid, dim3(SCAN_NT), 0, stream, a);
     else if (a.mode == WALK_BLOCKS)
-        hipLaunchKernelGGL((kda_affine_scan_mfma<DK, WALK_BLOCKS>), grid, dim3(SCAN_NT), 0, stream, a);
+        hipLaunchKernelGGL((kda_affine_scan_mfma<DK, WALK_BLOCKS, CT>), grid, dim3(SCAN_NT), 0, stream, a);
     else
-        hipLaunchKernelGGL((kda_affine_scan_mfma<DK, WALK_SEGMENTS>), grid, dim3(SCAN_NT), 0, stream, a);
+        hipLaunchKernelGGL((kda_affine_scan_mfma<DK, WALK_SEGMENTS, CT>), grid, dim3(SCAN_NT), 0, stream, a);
     return hipGetLastError();
+}
+
+// The blocks' segment walk takes 64-column workgroups when 16-column ones would number
+// four per CU or more (and the width allows it): at 256 segments x 8 heads it took 196
+// against 239 us.  The compose walk stays at 16 columns, whose two workgroups per CU
+// measured as fast or faster (87 against 97 us at 64 segments, 335 against 331 us at 256).
+template <int DK>
+static hipError_t launch_walk(const ScanWalk &a, hipStream_t stream) {
+    const int64_t wg16 = (int64_t)a.n_task * a.H * (a.width / 16);
+    if (a.mode == WALK_SEGMENTS && a.width % 64 == 0 && wg16 >= 4 * 256) return launch_walk_ct<DK, 4>(a, stream);
+    return launch_walk_ct<DK, 1>(a, stream);
 }
 
 static hipError_t launch_walk_dk(int dk, const ScanWalk &a, hipStream_t stream) {
@@ -283,7 +323,7 @@ hipError_t launch_affine_scan(int n_seg, int H, int dk, int dv, const float *M, 
 int scan_block_size(int n_seg, int dk, int dv, int blk) {
     if (blk <= 0) {
         // three launches and about three times the work: below 32 segments the ordered
-        // walk is faster (16 segments x 8 heads at dk = dv = 128: 0.056 against 0.080 ms);
+        // walk is faster (16 segments x 8 heads at dk = dv = 128: 0.054 against 0.080 ms);
         // above, a critical path of ~2 blk + n_seg / blk steps wants blk ~ sqrt(n_seg / 2)
         if (n_seg < 32) return n_seg;
         blk = 1;

@@ -218,7 +218,11 @@ def test_blocked_scan_scalar_example_exact():
 @pytest.mark.parametrize("dk,dv,n,H,block", [(128, 128, 48, 4, 0), (128, 128, 16, 8, 2), (128, 128, 17, 3, 5),
                                              (128, 64, 10, 2, 0), (64, 128, 7, 2, 3), (64, 64, 9, 3, 4),
                                              (64, 64, 40, 2, 0), (128, 128, 1, 2, 0), (128, 128, 6, 2, 6),
-                                             (32, 32, 40, 2, 3)])
+                                             (32, 32, 40, 2, 3),
+                                             # enough tasks for 64-column workgroups (compose
+                                             # and segment walks), square and both dk != dv
+                                             (128, 128, 200, 8, 0), (64, 64, 600, 8, 0),
+                                             (128, 64, 300, 8, 0), (64, 128, 300, 8, 0)])
 def test_blocked_scan_random_maps(dk, dv, n, H, block):
     from oracle import oracle as orc
     from kda_testlib import rel_fro
